@@ -1,0 +1,99 @@
+"""Mutation tests of the oracle: every deliberate mistake must fail a pin.
+
+[GAUDI] "Correctness" validates its converter the same way (seven deliberate
+mutations of the tool, each caught by at least one encoding test).  Here each
+mutant patches one piece of the oracle, then every argument-free pin test of
+the oracle suite runs; at least one must fail.
+"""
+
+import inspect
+
+import numpy as np
+import pytest
+
+import oracle.convert as OC
+import oracle.formats as OF
+import oracle.gemm as OG
+import oracle.quant as OQ
+import oracle.route as OR
+
+from . import (test_oracle_convert, test_oracle_formats, test_oracle_gemm,
+               test_oracle_quant, test_oracle_route_permute)
+
+_orig_unpack = OF.unpack_fp4
+_orig_e2m1 = OF.e2m1_decode
+_orig_floor = OF.floor_log2
+_orig_round = OF.round_to_grid
+_orig_silu = OG.silu_mul
+
+
+def _swap_nibbles(packed):
+    u = _orig_unpack(packed)
+    out = u.copy()
+    out[..., 0::2], out[..., 1::2] = u[..., 1::2], u[..., 0::2]
+    return out
+
+
+def _round_ties_away(x, mbits, emin, maxval, saturate):
+    r = _orig_round(x, mbits, emin, maxval, saturate)
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, emin)
+    q = np.ldexp(1.0, e - mbits)
+    tie = (a / q) % 1 == 0.5
+    up = np.copysign(np.minimum((np.floor(a / q) + 1) * q, maxval if saturate else np.inf), x)
+    return np.where(tie, up, r)
+
+
+def _order_desc_high_first(values):
+    idx = np.arange(len(values))
+    return np.lexsort((-idx, -values.astype(np.float64)))
+
+
+MUTANTS = {
+    "k = e_max - 6": [(OC, "TOP_EXPONENT", 6)],
+    "k = e_max - 8": [(OC, "TOP_EXPONENT", 8)],
+    "nibble order swapped": [(OF, "unpack_fp4", _swap_nibbles)],
+    "E2M1 sign dropped": [(OF, "e2m1_decode", lambda c: np.abs(_orig_e2m1(c)))],
+    "E8M0 bias 128": [(OF, "e8m0_decode", lambda s: np.where(
+        np.asarray(s) == 255, np.nan, np.ldexp(1.0, np.asarray(s, dtype=np.int64) - 128)))],
+    "floor(log2) off by one": [(OF, "floor_log2", lambda a: _orig_floor(a) + 1)],
+    "E8M0 255 not NaN": [(OF, "e8m0_decode", lambda s: np.ldexp(
+        1.0, np.asarray(s, dtype=np.int64) - 127))],
+    "RNE ties away from zero": [(OF, "round_to_grid", _round_ties_away)],
+    "MX scale uses emax 1": [(OQ, "E2M1_EMAX", 1)],
+    "routing ties to higher id": [(OR, "_order_desc", _order_desc_high_first)],
+    "gate/up swapped": [(OG, "silu_mul", lambda gu, I: _orig_silu(
+        np.concatenate([gu[:, I:], gu[:, :I]], axis=1), I))],
+}
+
+PIN_MODULES = [test_oracle_formats, test_oracle_convert, test_oracle_quant,
+               test_oracle_route_permute, test_oracle_gemm]
+
+
+def _pin_tests():
+    out = []
+    for m in PIN_MODULES:
+        for name, fn in sorted(vars(m).items()):
+            if name.startswith("test_") and callable(fn) and not inspect.signature(fn).parameters:
+                out.append((f"{m.__name__}.{name}", fn))
+    return out
+
+
+def test_pins_pass_unmutated():
+    for name, fn in _pin_tests():
+        fn()
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_mutant_is_killed(mutant, monkeypatch):
+    for mod, attr, val in MUTANTS[mutant]:
+        monkeypatch.setattr(mod, attr, val)
+    killed = []
+    for name, fn in _pin_tests():
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except Exception:
+            killed.append(name)
+    assert killed, f"mutant '{mutant}' survived every pin"
