@@ -1,0 +1,71 @@
+// moe_combine: weighted top-k combine of the stage-2 rows.
+//
+// [ATOM] "Stage D: MXFP4 Fused MoE": the stage-2 outputs of a token's expert
+// pairs are reduced into the token's output row.  [K3]: the shared-expert
+// contribution is added to the routed sum.
+// out[t] = bf16( sum_{j<topk} w[t,j] * y[pos(t,j)] + sum_i y[pos(t,topk+i)] ),
+// accumulated in float32 in ascending slot order (deterministic, no atomics).
+// Each lane owns 8 consecutive columns (16-byte loads and stores).
+#include "common.h"
+
+namespace fp4moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ y,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      const float* __restrict__ topk_w, int topk,
+                                                      int n_shared, int H,
+                                                      uint16_t* __restrict__ out,
+                                                      float* __restrict__ out_f32) {
+  const int64_t t = blockIdx.y;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (col >= H) return;
+  const int k = topk + n_shared;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const int p = pair_pos[t * k + j];
+    if (p < 0) continue;
+    const float w = (j < topk) ? topk_w[t * topk + j] : 1.f;
+    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)p * H + col);
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = fmaf(w, bf16_to_f32(u[i] & 0xffffu), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(w, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    }
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + t * H + col) = make_uint4(o[0], o[1], o[2], o[3]);
+  if (out_f32) {
+    float4* of = reinterpret_cast<float4*>(out_f32 + t * H + col);
+    of[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    of[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+  }
+}
+
+}  // namespace fp4moe
+
+using namespace fp4moe;
+
+extern "C" int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w,
+                           int T, int topk, int n_shared, int H, uint16_t* out, float* out_f32,
+                           void* stream) {
+  FP4MOE_REQUIRE(T >= 0 && topk >= 1 && n_shared >= 0 && H > 0 && H % 8 == 0,
+                 "moe_combine: T=%d topk=%d n_shared=%d H=%d (H %% 8 != 0)", T, topk, n_shared, H);
+  FP4MOE_REQUIRE(T <= 65535, "moe_combine: T=%d above 65535", T);
+  if (T == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(y_sorted && pair_pos && topk_w && out, "moe_combine: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)y_sorted & 15) == 0 && ((uintptr_t)out & 15) == 0 &&
+                     ((uintptr_t)out_f32 & 15) == 0,
+                 "moe_combine: y, out and out_f32 must be 16-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  const int lanes = H / 8;
+  dim3 grid((lanes + 255) / 256, T);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, as_stream(stream), y_sorted, pair_pos,
+                     topk_w, topk, n_shared, H, out, out_f32);
+  return check_launch("moe_combine");
+}

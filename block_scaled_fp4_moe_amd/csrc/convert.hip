@@ -1,0 +1,189 @@
+// mxfp4_to_fp8_channel: exact MXFP4 -> FP8 E4M3 per-channel conversion.
+//
+// [GAUDI] "Exact MXFP4 to FP8 per-channel conversion": per output row pick
+// one power-of-two channel scale 2^k with k = (exponent of the row's largest
+// element) - 7; each element becomes the E4M3 code of x / 2^k.  Rows whose
+// E8M0 scales span at most 9 binades convert exactly, every element an E4M3
+// normal with exponent in [-5, 7].
+//
+// The kernel is integer-only.  One wavefront converts one row in two passes
+// over its 16-byte blocks (one MX block per lane per step):
+//   pass 1: the largest element exponent of a block is its E8M0 exponent plus
+//           the exponent class of its largest E2M1 magnitude, found with a few
+//           bit tests on the packed nibbles; a wavefront max gives e_max.
+//   pass 2: within a block every element with magnitude code c maps to the
+//           same FP8 byte (sign aside), so the block's 8-entry byte table is
+//           built once and applied to 4 nibbles per v_perm_b32.
+#include "common.h"
+
+namespace fp4moe {
+
+constexpr int kNoElement = -100000;
+
+// Exponent class of the largest magnitude among the 8 nibbles of each word:
+// codes 6,7 -> 2; 4,5 -> 1; 2,3 -> 0; 1 -> -1; none -> kNoElement.
+__device__ __forceinline__ int block_max_class(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  const uint32_t m0 = w0 & 0x77777777u, m1 = w1 & 0x77777777u, m2 = w2 & 0x77777777u,
+                 m3 = w3 & 0x77777777u;
+  const uint32_t any = m0 | m1 | m2 | m3;
+  const uint32_t six = ((m0 & (m0 << 1)) | (m1 & (m1 << 1)) | (m2 & (m2 << 1)) |
+                        (m3 & (m3 << 1))) & 0x44444444u;
+  if (six) return 2;
+  if (any & 0x44444444u) return 1;
+  if (any & 0x22222222u) return 0;
+  if (any & 0x11111111u) return -1;
+  return kNoElement;
+}
+
+// FP8 byte of the E2M1 magnitude code c (1..7) scaled by 2^d, with flags.
+// value = sig * 2^(cls + d), sig in {1, 1.5}.
+__device__ __forceinline__ uint32_t fp8_of_mag(int c, int d, bool* inexact, bool* below) {
+  const int cls = (c >> 1) - 1;           // 1 -> -1, 2,3 -> 0, 4,5 -> 1, 6,7 -> 2
+  const bool half = (c == 3) || (c == 5) || (c == 7);
+  const int E = cls + d;
+  *below = E < -5;
+  *inexact = false;
+  if (E >= -6) return ((uint32_t)(E + 7) << 3) | (half ? 4u : 0u);
+  // E4M3 subnormal: value in units of 2^-9, round half to even.
+  const int sh = E + 9;                   // units = sig * 2^sh, sh <= 2
+  if (sh <= -2) {                         // below a quarter unit: rounds to zero
+    *inexact = true;
+    return 0u;
+  }
+  float units = (half ? 1.5f : 1.0f) * ldexpf(1.0f, sh);
+  const float r = rintf(units);
+  *inexact = (r != units);
+  return (uint32_t)r;
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+__global__ __launch_bounds__(256) void mx_to_fp8_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        int64_t rows, int K,
+                                                        uint8_t* __restrict__ fp8,
+                                                        float* __restrict__ channel_scale,
+                                                        uint8_t* __restrict__ row_status,
+                                                        uint32_t* __restrict__ n_inexact) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int nblk = K / 32;
+  const uint8_t* crow = codes + row * (K / 2);
+  const uint8_t* srow = scales + row * nblk;
+  uint8_t* orow = fp8 + row * K;
+
+  // pass 1: e_max over finite blocks
+  int emax = kNoElement;
+  bool has_nan = false;
+  for (int b = lane; b < nblk; b += 64) {
+    const int s = srow[b];
+    if (s == 255) {
+      has_nan = true;
+      continue;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(crow + b * 16);
+    const int cls = block_max_class(w.x, w.y, w.z, w.w);
+    if (cls != kNoElement) emax = max(emax, s - 127 + cls);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+  const bool zero_row = (emax == kNoElement);
+  const int k = zero_row ? 0 : emax - 7;
+
+  // pass 2: encode
+  bool any_below = false, any_inexact = false;
+  for (int b = lane; b < nblk; b += 64) {
+    const int s = srow[b];
+    uint4* dst = reinterpret_cast<uint4*>(orow + b * 32);
+    if (s == 255) {
+      const uint4 nanv = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
+      dst[0] = nanv;
+      dst[1] = nanv;
+      continue;
+    }
+    const uint4 w = *reinterpret_cast<const uint4*>(crow + b * 16);
+    const int d = s - 127 - k;
+    // table bytes 0..7 for magnitude codes 0..7
+    uint32_t lut_lo = 0, lut_hi = 0;
+    uint32_t below_mask = 0, inexact_mask = 0;
+    if (d >= -4) {
+      // fast path: every class lands on a normal with exponent >= -5, exact
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        const int cls = (c >> 1) - 1;
+        const uint32_t byte = ((uint32_t)(cls + d + 7) << 3) | ((c & 1) && c > 1 ? 4u : 0u);
+        if (c < 4) lut_lo |= byte << (8 * c);
+        else lut_hi |= byte << (8 * (c - 4));
+      }
+    } else {
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        bool inex, below;
+        const uint32_t byte = fp8_of_mag(c, d, &inex, &below);
+        if (c < 4) lut_lo |= byte << (8 * c);
+        else lut_hi |= byte << (8 * (c - 4));
+        below_mask |= (below ? 1u : 0u) << c;
+        inexact_mask |= (inex ? 1u : 0u) << c;
+      }
+    }
+    const uint32_t win[4] = {w.x, w.y, w.z, w.w};
+    uint32_t out[8];
+    uint32_t present = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // bytes [b0,b0,b1,b1] and [b2,b2,b3,b3], then keep lo/hi nibble alternately
+      const uint32_t t0 = __builtin_amdgcn_perm(win[i], win[i], 0x01010000u);
+      const uint32_t t1 = __builtin_amdgcn_perm(win[i], win[i], 0x03030202u);
+      const uint32_t x0 = (t0 & 0x000f000fu) | ((t0 >> 4) & 0x0f000f00u);
+      const uint32_t x1 = (t1 & 0x000f000fu) | ((t1 >> 4) & 0x0f000f00u);
+      out[2 * i] = __builtin_amdgcn_perm(lut_hi, lut_lo, x0 & 0x07070707u) |
+                   ((x0 & 0x08080808u) << 4);
+      out[2 * i + 1] = __builtin_amdgcn_perm(lut_hi, lut_lo, x1 & 0x07070707u) |
+                       ((x1 & 0x08080808u) << 4);
+      if (below_mask | inexact_mask) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) present |= 1u << ((win[i] >> (4 * n)) & 7u);
+      }
+    }
+    any_below |= (present & below_mask) != 0;
+    any_inexact |= (present & inexact_mask) != 0;
+    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  }
+  has_nan = __ballot(has_nan) != 0;
+  any_below = __ballot(any_below) != 0;
+  any_inexact = __ballot(any_inexact) != 0;
+  if (lane == 0) {
+    channel_scale[row] = ldexpf(1.0f, k);
+    if (row_status) {
+      row_status[row] = has_nan ? 2 : (zero_row ? 3 : (any_below ? 1 : 0));
+    }
+    if (any_inexact) atomicAdd(n_inexact, 1u);
+  }
+}
+
+}  // namespace fp4moe
+
+using namespace fp4moe;
+
+extern "C" int mxfp4_to_fp8_channel(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                    int K, uint8_t* fp8, float* channel_scale,
+                                    uint8_t* row_status, uint32_t* n_inexact_rows, void* stream) {
+  FP4MOE_REQUIRE(rows >= 0 && K > 0 && K % 32 == 0,
+                 "mxfp4_to_fp8_channel: rows=%lld K=%d (K %% 32 != 0)", (long long)rows, K);
+  FP4MOE_REQUIRE(n_inexact_rows, "mxfp4_to_fp8_channel: n_inexact_rows is required");
+  FP4MOE_REQUIRE(rows == 0 || (codes && scales && fp8 && channel_scale),
+                 "mxfp4_to_fp8_channel: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)codes & 15) == 0 && ((uintptr_t)fp8 & 15) == 0,
+                 "mxfp4_to_fp8_channel: codes and fp8 must be 16-byte aligned");
+  FP4MOE_REQUIRE((rows + 3) / 4 < (1ll << 31), "mxfp4_to_fp8_channel: too many rows");
+  FP4MOE_CHECK_DEVICE();
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, n_inexact_rows);
+  if (rows > 0) {
+    hipLaunchKernelGGL(mx_to_fp8_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, codes,
+                       scales, rows, K, fp8, channel_scale, row_status, n_inexact_rows);
+  }
+  return check_launch("mxfp4_to_fp8_channel");
+}

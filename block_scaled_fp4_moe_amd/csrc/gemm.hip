@@ -1,0 +1,528 @@
+// fp4_grouped_gemm: one expert-grouped GEMM stage of the MoE layer on gfx950.
+//
+// [ATOM] "Stage D: MXFP4 Fused MoE": two stages, stage 1 on the fused gate/up
+// weights, stage 2 on the down weights.  [ATOM] "When Is the Scale Applied?":
+// for bf16 activations the block scale is absorbed while decoding the weight
+// before a bf16 MFMA; for FP4 activations the payloads and E8M0 scales go
+// straight into the gfx950 scaled MFMA.  [NVFP4] "Memory Management": the MoE
+// path fuses dequantization into the GEMM tile, no bf16 weight buffer is
+// staged in memory.  [GAUDI] "What was built": gate and up rows are
+// concatenated in one fused tensor (gate first, by our reading).
+//
+// Operand layout (both MFMA families): in a 16x16 MFMA tile lane l holds one
+// 32-element MX block of row (l % 16), block index (l / 16) of the current
+// 128-wide K chunk.  In the natural row-major [N, K/2] layout that is exactly
+// one aligned 16-byte load per lane, with the four lanes of a row reading 64
+// contiguous bytes, and its scale is one byte -- no shuffling and no LDS for
+// the weights.  The accumulator of lane l holds rows 4*(l/16)..+3 (tokens) of
+// column l % 16 (weight row).
+//
+// Families
+//   dq  (afmt BF16; wfmt MXFP4 | NVFP4): weights decoded to bf16 in registers
+//       (v_cvt_scalef32_pk_*_fp4), v_mfma_f32_16x16x32_bf16.  A workgroup is
+//       four waves that split the K chunks round-robin and reduce through LDS,
+//       so even a single decode token spreads an expert over many CUs.
+//   mx  (afmt MXFP4; wfmt MXFP4 | FP8): v_mfma_scale_f32_16x16x128_f8f6f4 with
+//       the E8M0 bytes as scale operands; FP8 weights carry a per-row float
+//       channel scale applied in the epilogue.
+#include "common.h"
+
+namespace fp4moe {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+struct GemmParams {
+  int N, K, n_experts, block_m, gather_div;
+  int64_t lda, ldo;
+  const uint8_t* w;
+  const uint8_t* w_scale;
+  const float* w_tensor_scale;
+  const float* w_channel_scale;
+  const void* a;
+  const uint8_t* a_scale;
+  const int32_t* gather;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  uint16_t* out;
+  float* out_f32;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+__device__ __forceinline__ v8bf cat8(v2bf a, v2bf b, v2bf c, v2bf d) {
+  const v4bf lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const v4bf hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E4M3FN byte -> float (finite codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Eight bf16 weights (elements 8s..8s+7 of the lane's block) from dword `d`
+// of the 16-byte E2M1 payload, times an E8M0 scale given as float.
+__device__ __forceinline__ v8bf decode_mx8(uint32_t d, float scale) {
+  return cat8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3));
+}
+
+// Same for NVFP4: E2M1 times an arbitrary E4M3 scale.  The product has at
+// most 6 significant bits, so it is exact in bf16.
+__device__ __forceinline__ v2bf nv_pair(uint32_t d, float scale, int sel) {
+  v2f f;
+  switch (sel) {
+    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2); break;
+    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3); break;
+  }
+  v2bf r;
+  r[0] = (__bf16)(f[0] * scale);
+  r[1] = (__bf16)(f[1] * scale);
+  return r;
+}
+
+__device__ __forceinline__ v8bf decode_nv8(uint32_t d, float scale) {
+  return cat8(nv_pair(d, scale, 0), nv_pair(d, scale, 1), nv_pair(d, scale, 2),
+              nv_pair(d, scale, 3));
+}
+
+__device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+// ===========================================================================
+// dq family: bf16 activations, FP4 weights decoded in registers
+// ===========================================================================
+
+template <int WFMT, int STAGE, int MB>
+__global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
+  constexpr int NG = 2;            // two 16-row weight groups per work item
+  constexpr int NV = MB * NG * 4;  // accumulator floats per lane
+  __shared__ float red[3][NV][64];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int BM = MB * 16;
+  const int n_nb = (STAGE == 1) ? (p.N / 2) / 16 : p.N / 32;
+  const int nkc = p.K / 128;
+  const int64_t wrow_bytes = p.K / 2;
+  const int64_t srow_bytes = (WFMT == FP4MOE_W_MXFP4) ? p.K / 32 : p.K / 16;
+  const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
+  const uint16_t* A = static_cast<const uint16_t*>(p.a);
+
+  for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+    const int tile = (int)(wi / n_nb), nb = (int)(wi - (int64_t)tile * n_nb);
+    const int e = p.tiles[2 * tile], mt = p.tiles[2 * tile + 1];
+    const int row0 = p.offsets[e] + mt * BM;
+    const int row_end = min(p.offsets[e + 1], row0 + BM);
+
+    const uint8_t* wp[NG];
+    const uint8_t* sp[NG];
+#pragma unroll
+    for (int ng = 0; ng < NG; ++ng) {
+      const int wr = (STAGE == 1) ? (ng * (p.N / 2) + nb * 16 + r16) : (nb * 32 + ng * 16 + r16);
+      const int64_t row = (int64_t)e * p.N + wr;
+      wp[ng] = p.w + row * wrow_bytes;
+      sp[ng] = p.w_scale + row * srow_bytes;
+    }
+    const uint16_t* ap[MB];
+    bool av[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = row0 + mb * 16 + r16;
+      av[mb] = r < row_end;
+      int64_t arow = r;
+      if (av[mb] && p.gather) arow = p.gather[r] / p.gather_div;
+      ap[mb] = A + arow * p.lda;
+    }
+
+    v4f acc[MB][NG];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) acc[mb][ng] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = wave; c < nkc; c += 4) {
+      const int blk = c * 4 + g;
+      uint4 wv[NG];
+      float sc[NG][2];
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        wv[ng] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 16);
+        if (WFMT == FP4MOE_W_MXFP4) {
+          sc[ng][0] = __uint_as_float((uint32_t)sp[ng][blk] << 23);
+          sc[ng][1] = sc[ng][0];
+        } else {
+          const uint32_t two = *reinterpret_cast<const uint16_t*>(sp[ng] + blk * 2);
+          sc[ng][0] = e4m3_to_f32(two & 0xffu);
+          sc[ng][1] = e4m3_to_f32(two >> 8);
+        }
+      }
+      uint4 a4[MB][4];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          a4[mb][s] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 32 + s * 8)
+                             : make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v8bf b[NG];
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng) {
+          const uint32_t d = (s == 0) ? wv[ng].x : (s == 1) ? wv[ng].y : (s == 2) ? wv[ng].z : wv[ng].w;
+          b[ng] = (WFMT == FP4MOE_W_MXFP4) ? decode_mx8(d, sc[ng][0]) : decode_nv8(d, sc[ng][s >> 1]);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const v8bf a = as_bf8(a4[mb][s]);
+#pragma unroll
+          for (int ng = 0; ng < NG; ++ng)
+            acc[mb][ng] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ng], acc[mb][ng], 0, 0, 0);
+        }
+      }
+    }
+
+    // K reduction over the four waves, in wave order.
+    if (wave > 0) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) red[wave - 1][(mb * NG + ng) * 4 + i][lane] = acc[mb][ng][i];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 0; w < 3; ++w)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int ng = 0; ng < NG; ++ng)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mb][ng][i] += red[w][(mb * NG + ng) * 4 + i][lane];
+      const float ts = (WFMT == FP4MOE_W_NVFP4) ? p.w_tensor_scale[e] : 1.0f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + mb * 16 + g * 4 + i;
+          if (r >= row_end) continue;
+          if (STAGE == 1) {
+            const float h = silu_mul(acc[mb][0][i] * ts, acc[mb][1][i] * ts);
+            const int64_t o = (int64_t)r * p.ldo + nb * 16 + r16;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(h);
+            if (p.out_f32) p.out_f32[o] = h;
+          } else {
+#pragma unroll
+            for (int ng = 0; ng < NG; ++ng) {
+              const float y = acc[mb][ng][i] * ts;
+              const int64_t o = (int64_t)r * p.ldo + nb * 32 + ng * 16 + r16;
+              p.out[o] = (uint16_t)f32_to_bf16_rne(y);
+              if (p.out_f32) p.out_f32[o] = y;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ===========================================================================
+// mx family: MXFP4 activations, scaled MFMA FP4 x (FP4 | FP8)
+// ===========================================================================
+
+// Waves form a 2 x 2 grid over the workgroup tile; each wave owns WM M-blocks
+// and WN weight-row blocks of 16.  Stage 1 pairs gate block j with up block
+// j + WN/2 so SiLU(gate)*up is lane-local.
+template <int WFMT, int STAGE, int WM, int WN>
+__global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int BM = 2 * WM * 16;
+  constexpr int OUT_PER_WAVE = (STAGE == 1) ? (WN / 2) * 16 : WN * 16;  // output columns
+  constexpr int OUT_PER_WG = 2 * OUT_PER_WAVE;
+  const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
+  const int n_nb = n_out / OUT_PER_WG;
+  const int nkc = p.K / 128;
+  const int64_t wrow_bytes = (WFMT == FP4MOE_W_FP8) ? p.K : p.K / 2;
+  const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
+  const uint8_t* A = static_cast<const uint8_t*>(p.a);
+  const int64_t a_row_bytes = p.lda / 2, a_srow = p.lda / 32;
+
+  for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
+    const int tile = (int)(wi / n_nb), nb = (int)(wi - (int64_t)tile * n_nb);
+    const int e = p.tiles[2 * tile], mt = p.tiles[2 * tile + 1];
+    const int row0 = p.offsets[e] + mt * BM + wm * WM * 16;
+    const int row_end = min(p.offsets[e + 1], p.offsets[e] + (mt + 1) * BM);
+    const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE;   // first output column of this wave
+
+    const uint8_t* ap[WM];
+    const uint8_t* asp[WM];
+    bool av[WM];
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) {
+      const int r = row0 + mb * 16 + r16;
+      av[mb] = r < row_end;
+      int64_t arow = r;
+      if (av[mb] && p.gather) arow = p.gather[r] / p.gather_div;
+      if (!av[mb]) arow = 0;
+      ap[mb] = A + arow * a_row_bytes;
+      asp[mb] = p.a_scale + arow * a_srow;
+    }
+    const uint8_t* wp[WN];
+    const uint8_t* sp[WN];
+    int wrow[WN];
+#pragma unroll
+    for (int nbk = 0; nbk < WN; ++nbk) {
+      int wr;
+      if (STAGE == 1) {
+        wr = (nbk < WN / 2) ? (col0 + nbk * 16 + r16) : (p.N / 2 + col0 + (nbk - WN / 2) * 16 + r16);
+      } else {
+        wr = col0 + nbk * 16 + r16;
+      }
+      wrow[nbk] = wr;
+      const int64_t row = (int64_t)e * p.N + wr;
+      wp[nbk] = p.w + row * wrow_bytes;
+      sp[nbk] = (WFMT == FP4MOE_W_MXFP4) ? p.w_scale + row * (p.K / 32) : nullptr;
+    }
+
+    v4f acc[WM][WN];
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+      for (int nbk = 0; nbk < WN; ++nbk) acc[mb][nbk] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = 0; c < nkc; ++c) {
+      const int blk = c * 4 + g;
+      v8i af[WM];
+      int as[WM];
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        int s = 127;
+        if (av[mb]) {
+          v = *reinterpret_cast<const uint4*>(ap[mb] + blk * 16);
+          s = asp[mb][blk];
+        }
+        af[mb] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        as[mb] = s;
+      }
+      v8i bf[WN];
+      int bs[WN];
+#pragma unroll
+      for (int nbk = 0; nbk < WN; ++nbk) {
+        if (WFMT == FP4MOE_W_MXFP4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 16);
+          bf[nbk] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+          bs[nbk] = sp[nbk][blk];
+        } else {
+          const uint4 v0 = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 32);
+          const uint4 v1 = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 32 + 16);
+          bf[nbk] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+          bs[nbk] = 127;
+        }
+      }
+#pragma unroll
+      for (int mb = 0; mb < WM; ++mb)
+#pragma unroll
+        for (int nbk = 0; nbk < WN; ++nbk) {
+          if (WFMT == FP4MOE_W_MXFP4)
+            acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[mb], bf[nbk], acc[mb][nbk], 4, 4, 0, as[mb], 0, bs[nbk]);
+          else
+            acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[mb], bf[nbk], acc[mb][nbk], 4, 0, 0, as[mb], 0, bs[nbk]);
+        }
+    }
+
+    // epilogue
+    float cs[WN];
+#pragma unroll
+    for (int nbk = 0; nbk < WN; ++nbk)
+      cs[nbk] = (WFMT == FP4MOE_W_FP8) ? p.w_channel_scale[(int64_t)e * p.N + wrow[nbk]] : 1.0f;
+#pragma unroll
+    for (int mb = 0; mb < WM; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + mb * 16 + g * 4 + i;
+        if (r >= row_end) continue;
+        if (STAGE == 1) {
+#pragma unroll
+          for (int j = 0; j < WN / 2; ++j) {
+            const float h = silu_mul(acc[mb][j][i] * cs[j], acc[mb][j + WN / 2][i] * cs[j + WN / 2]);
+            const int64_t o = (int64_t)r * p.ldo + col0 + j * 16 + r16;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(h);
+            if (p.out_f32) p.out_f32[o] = h;
+          }
+        } else {
+#pragma unroll
+          for (int nbk = 0; nbk < WN; ++nbk) {
+            const float y = acc[mb][nbk][i] * cs[nbk];
+            const int64_t o = (int64_t)r * p.ldo + col0 + nbk * 16 + r16;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(y);
+            if (p.out_f32) p.out_f32[o] = y;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ===========================================================================
+// dispatch
+// ===========================================================================
+
+static int g_num_cus = 0;
+
+static int grid_cap() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    g_num_cus = n;
+  }
+  return g_num_cus * 8;
+}
+
+template <int WFMT, int STAGE>
+static void launch_dq(const GemmParams& p, int max_tiles, hipStream_t s) {
+  const int n_nb = (STAGE == 1) ? (p.N / 2) / 16 : p.N / 32;
+  int64_t work = (int64_t)max_tiles * n_nb;
+  const int grid = (int)(work < grid_cap() ? (work < 1 ? 1 : work) : grid_cap());
+  switch (p.block_m) {
+    case 16: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 1>), dim3(grid), dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 4>), dim3(grid), dim3(256), 0, s, p); break;
+  }
+}
+
+template <int WFMT, int STAGE, int WM>
+static void launch_mx_wm(const GemmParams& p, int max_tiles, hipStream_t s) {
+  constexpr int WN = 4;
+  const int out_per_wg = 2 * ((STAGE == 1) ? (WN / 2) * 16 : WN * 16);
+  const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
+  const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
+  const int grid = (int)(work < grid_cap() ? (work < 1 ? 1 : work) : grid_cap());
+  hipLaunchKernelGGL((mx_gemm_kernel<WFMT, STAGE, WM, WN>), dim3(grid), dim3(256), 0, s, p);
+}
+
+template <int WFMT, int STAGE>
+static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
+  switch (p.block_m) {
+    case 32: launch_mx_wm<WFMT, STAGE, 1>(p, max_tiles, s); break;
+    case 64: launch_mx_wm<WFMT, STAGE, 2>(p, max_tiles, s); break;
+    case 128: launch_mx_wm<WFMT, STAGE, 4>(p, max_tiles, s); break;
+    default: launch_mx_wm<WFMT, STAGE, 8>(p, max_tiles, s); break;
+  }
+}
+
+}  // namespace fp4moe
+
+using namespace fp4moe;
+
+extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
+  FP4MOE_REQUIRE(a, "fp4_grouped_gemm: null args");
+  FP4MOE_REQUIRE(a->stage == 1 || a->stage == 2, "fp4_grouped_gemm: stage=%d", a->stage);
+  const bool dq = a->afmt == FP4MOE_A_BF16;
+  const bool mx = a->afmt == FP4MOE_A_MXFP4;
+  FP4MOE_REQUIRE((dq && (a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4)) ||
+                     (mx && (a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_FP8)),
+                 "fp4_grouped_gemm: unsupported (wfmt=%d, afmt=%d)", a->wfmt, a->afmt);
+  FP4MOE_REQUIRE(a->K > 0 && a->K % 128 == 0, "fp4_grouped_gemm: K=%d not a multiple of 128", a->K);
+  FP4MOE_REQUIRE(a->N > 0 && a->N % 32 == 0 && (a->stage == 2 || a->N % 64 == 0),
+                 "fp4_grouped_gemm: N=%d (stage %d)", a->N, a->stage);
+  if (dq) {
+    FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64,
+                   "fp4_grouped_gemm: block_m=%d not in {16,32,64} for bf16 activations",
+                   a->block_m);
+  } else {
+    FP4MOE_REQUIRE(a->block_m == 32 || a->block_m == 64 || a->block_m == 128 || a->block_m == 256,
+                   "fp4_grouped_gemm: block_m=%d not in {32,64,128,256} for MXFP4 activations",
+                   a->block_m);
+    const int out_per_wg = a->stage == 1 ? 64 : 128;
+    const int n_out = a->stage == 1 ? a->N / 2 : a->N;
+    FP4MOE_REQUIRE(n_out % out_per_wg == 0,
+                   "fp4_grouped_gemm: output width %d not a multiple of %d", n_out, out_per_wg);
+  }
+  FP4MOE_REQUIRE(a->n_experts >= 1 && a->max_rows >= 0 && a->max_tiles >= 0,
+                 "fp4_grouped_gemm: n_experts=%d max_rows=%d max_tiles=%d", a->n_experts,
+                 a->max_rows, a->max_tiles);
+  FP4MOE_REQUIRE(a->gather_div >= 1, "fp4_grouped_gemm: gather_div=%d", a->gather_div);
+  const int n_out = a->stage == 1 ? a->N / 2 : a->N;
+  FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
+  FP4MOE_REQUIRE(a->lda >= a->K && a->lda % 32 == 0, "fp4_grouped_gemm: lda=%lld",
+                 (long long)a->lda);
+  if (a->max_tiles == 0 || a->max_rows == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(a->w && a->a && a->expert_offsets && a->tiles && a->n_tiles && a->out,
+                 "fp4_grouped_gemm: null pointer");
+  FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_FP8 || a->w_scale, "fp4_grouped_gemm: w_scale is null");
+  FP4MOE_REQUIRE(a->wfmt != FP4MOE_W_NVFP4 || a->w_tensor_scale,
+                 "fp4_grouped_gemm: NVFP4 needs w_tensor_scale");
+  FP4MOE_REQUIRE(a->wfmt != FP4MOE_W_FP8 || a->w_channel_scale,
+                 "fp4_grouped_gemm: FP8 needs w_channel_scale");
+  FP4MOE_REQUIRE(!mx || a->a_scale, "fp4_grouped_gemm: MXFP4 activations need a_scale");
+  FP4MOE_REQUIRE(((uintptr_t)a->w & 15) == 0 && ((uintptr_t)a->a & 15) == 0,
+                 "fp4_grouped_gemm: w and a must be 16-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+
+  GemmParams p;
+  p.N = a->N;
+  p.K = a->K;
+  p.n_experts = a->n_experts;
+  p.block_m = a->block_m;
+  p.gather_div = a->gather_div;
+  p.lda = a->lda;
+  p.ldo = a->ldo;
+  p.w = a->w;
+  p.w_scale = a->w_scale;
+  p.w_tensor_scale = a->w_tensor_scale;
+  p.w_channel_scale = a->w_channel_scale;
+  p.a = a->a;
+  p.a_scale = a->a_scale;
+  p.gather = a->a_row_gather;
+  p.offsets = a->expert_offsets;
+  p.tiles = a->tiles;
+  p.n_tiles = a->n_tiles;
+  p.out = a->out;
+  p.out_f32 = a->out_f32;
+  hipStream_t s = as_stream(stream);
+  const int mt = a->max_tiles;
+  if (dq) {
+    if (a->wfmt == FP4MOE_W_MXFP4) {
+      if (a->stage == 1) launch_dq<FP4MOE_W_MXFP4, 1>(p, mt, s);
+      else launch_dq<FP4MOE_W_MXFP4, 2>(p, mt, s);
+    } else {
+      if (a->stage == 1) launch_dq<FP4MOE_W_NVFP4, 1>(p, mt, s);
+      else launch_dq<FP4MOE_W_NVFP4, 2>(p, mt, s);
+    }
+  } else {
+    if (a->wfmt == FP4MOE_W_MXFP4) {
+      if (a->stage == 1) launch_mx<FP4MOE_W_MXFP4, 1>(p, mt, s);
+      else launch_mx<FP4MOE_W_MXFP4, 2>(p, mt, s);
+    } else {
+      if (a->stage == 1) launch_mx<FP4MOE_W_FP8, 1>(p, mt, s);
+      else launch_mx<FP4MOE_W_FP8, 2>(p, mt, s);
+    }
+  }
+  return check_launch("fp4_grouped_gemm");
+}

@@ -1,0 +1,252 @@
+// Dynamic activation quantization: mxfp4_quant_1x32 and nvfp4_qdq.
+//
+// mxfp4_quant_1x32 -- [ATOM] "Stage B: Dynamic Activation Quantization":
+// bf16 activations become E2M1 payloads plus one E8M0 scale per 32 values.
+// Scale rule (OCP MX): e = floor(log2 amax) - 2, clamped at -127.  For a bf16
+// amax with biased exponent field f this is simply scale byte = max(f - 2, 0),
+// so the scale is pure integer work on the bf16 bits.
+//
+// nvfp4_qdq -- [NVFP4] "Weight Dequantization and Activation QDQ":
+// quantize-dequantize round trip before each GEMM; every step is an IEEE
+// float32 operation with round-to-nearest-even.
+//
+// Layout: each lane owns 8 consecutive bf16 (one 16-byte load), so 4 lanes
+// cover an MX block and 2 lanes an NVFP4 block; block maxima are combined
+// with xor shuffles.  Loads and stores are 16 B per lane, fully coalesced.
+#include "common.h"
+
+namespace fp4moe {
+
+// E2M1 code magnitude (0..7) of |q| by round-to-nearest-even on the grid
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6: ties 0.25, 1.25, 2.5, 5 go
+// down and 0.75, 1.75, 3.5 go up, always to the even code.
+__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
+  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+         (uint32_t)(a > 5.0f);
+}
+
+__device__ __forceinline__ float e2m1_mag_value(uint32_t c) {
+  // codes 0..7 -> 0, .5, 1, 1.5, 2, 3, 4, 6
+  return c < 4 ? 0.5f * (float)c : (c == 7 ? 6.0f : (float)(c - 2));
+}
+
+// floor(log2 v) for a positive normal float.
+__device__ __forceinline__ int floor_log2_f32(float v) {
+  return (int)((__float_as_uint(v) >> 23) & 0xffu) - 127;
+}
+
+// Round a non-negative finite float to the nearest E4M3FN value (ties to
+// even, saturating at 448).  Returns the value; *code receives the byte.
+__device__ __forceinline__ float e4m3_rne_sat(float v, uint32_t* code) {
+  if (!(v > 0.f)) {
+    *code = 0;
+    return 0.f;
+  }
+  if (v >= 448.f) {
+    *code = 0x7e;
+    return 448.f;
+  }
+  int e = (__float_as_uint(v) >> 23) == 0 ? -127 : floor_log2_f32(v);
+  e = max(e, -6);
+  const int qe = e - 3;                       // quantum 2^(e-3): 3 mantissa bits
+  float r = rintf(v * exp2i(-qe)) * exp2i(qe);  // both scalings are exact
+  r = fminf(r, 448.f);
+  if (r == 0.f) {
+    *code = 0;
+  } else if (r >= 0.015625f) {
+    const int E = floor_log2_f32(r);
+    const uint32_t mant = (uint32_t)((r * exp2i(-E) - 1.f) * 8.f);
+    *code = ((uint32_t)(E + 7) << 3) | mant;
+  } else {
+    *code = (uint32_t)(r * 512.f);            // subnormal: r = m * 2^-9
+  }
+  return r;
+}
+
+// ---- mxfp4_quant_1x32 ---------------------------------------------------
+
+__global__ __launch_bounds__(256) void mxfp4_quant_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ row_count, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int chunks_per_row = K / 8;
+  const int64_t total = (int64_t)M * chunks_per_row;
+  const int rows = row_count ? min(M, *row_count) : M;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c - threadIdx.x % 4 < total;
+       c += stride) {
+    const int64_t row = c / chunks_per_row;
+    const int cr = (int)(c - row * chunks_per_row);
+    const bool active = c < total && row < rows;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (active) {
+      const int64_t src = gather ? (int64_t)gather[row] : row;
+      v = *reinterpret_cast<const uint4*>(x + src * ldx + (int64_t)cr * 8);
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = max(amax, w[i] & 0x7fffu);
+      amax = max(amax, (w[i] >> 16) & 0x7fffu);
+    }
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+    const int f = (int)(amax >> 7);                 // bf16 biased exponent of amax
+    const uint32_t sbyte = (uint32_t)max(f - 2, 0);
+    const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^(127 - sbyte) = 2^-e
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      const float q = bf16_to_f32(h & 0x7fffu) * inv;
+      const uint32_t code = e2m1_mag_code(q) | ((h >> 12) & 8u);
+      packed |= code << (4 * i);
+    }
+    if (active) {
+      *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + (int64_t)cr * 4) = packed;
+      if ((cr & 3) == 0) scales[row * (K / 32) + cr / 4] = (uint8_t)sbyte;
+    }
+  }
+}
+
+// ---- nvfp4_qdq ----------------------------------------------------------
+
+__global__ void nvfp4_zero_kernel(uint32_t* ws) { ws[0] = 0u; }
+
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* __restrict__ x, int M,
+                                                         int K, const int32_t* __restrict__ row_count,
+                                                         uint32_t* __restrict__ ws) {
+  const int rows = row_count ? min(M, *row_count) : M;
+  const int64_t total = (int64_t)rows * (K / 8);
+  uint32_t amax = 0;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = max(amax, w[i] & 0x7fffu);
+      amax = max(amax, (w[i] >> 16) & 0x7fffu);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
+  if ((threadIdx.x & 63) == 0 && amax) atomicMax(ws, amax);
+}
+
+__global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
+    const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ row_count,
+    const float* __restrict__ ts_in, const uint32_t* __restrict__ ws, uint16_t* __restrict__ y,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+  float s_t;
+  if (ts_in) {
+    s_t = *ts_in;
+  } else {
+    const float amax_t = bf16_to_f32(*ws);
+    s_t = amax_t > 0.f ? __fdiv_rn(amax_t, 2688.f) : 1.f;
+  }
+  if (ts_out && blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  const float denom = __fmul_rn(6.f, s_t);
+  const int rows = row_count ? min(M, *row_count) : M;
+  const int64_t total = (int64_t)rows * (K / 8);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c - threadIdx.x % 2 < total;
+       c += stride) {
+    const bool active = c < total;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (active) v = reinterpret_cast<const uint4*>(x)[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      amax = max(amax, w[i] & 0x7fffu);
+      amax = max(amax, (w[i] >> 16) & 0x7fffu);
+    }
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
+    uint32_t scode;
+    const float sb = e4m3_rne_sat(__fdiv_rn(bf16_to_f32(amax), denom), &scode);
+    const float d = __fmul_rn(sb, s_t);
+    uint32_t packed = 0;
+    uint32_t yo[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      const uint32_t sign = (h >> 15) & 1u;
+      uint32_t mag = 0;
+      uint32_t ybits = sign << 15;
+      if (sb > 0.f) {
+        const float q = __fdiv_rn(bf16_to_f32(h), d);
+        mag = e2m1_mag_code(fabsf(q));
+        const float qv = __fmul_rn(e2m1_mag_value(mag), sb);   // exact
+        const float yv = __fmul_rn(sign ? -qv : qv, s_t);
+        ybits = f32_to_bf16_rne(yv);
+        if (mag == 0) ybits = sign << 15;
+      }
+      packed |= (mag | (sign << 3)) << (4 * i);
+      yo[i >> 1] |= ybits << (16 * (i & 1));
+    }
+    if (active) {
+      reinterpret_cast<uint4*>(y)[c] = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+      if (codes) reinterpret_cast<uint32_t*>(codes)[c] = packed;
+      if (scales && (c & 1) == 0) scales[c / 2] = (uint8_t)scode;
+    }
+  }
+}
+
+static int grid_for(int64_t work_items, int per_block) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g > 256 * 32) g = 256 * 32;
+  return g < 1 ? 1 : (int)g;
+}
+
+}  // namespace fp4moe
+
+using namespace fp4moe;
+
+extern "C" int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx,
+                                const int32_t* row_gather, const int32_t* row_count,
+                                uint8_t* codes, uint8_t* scales, void* stream) {
+  FP4MOE_REQUIRE(M >= 0 && K > 0 && K % 32 == 0, "mxfp4_quant_1x32: M=%d K=%d (K %% 32 != 0)",
+                 M, K);
+  FP4MOE_REQUIRE(ldx >= K && ldx % 8 == 0, "mxfp4_quant_1x32: ldx=%lld", (long long)ldx);
+  if (M == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(x && codes && scales, "mxfp4_quant_1x32: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 3) == 0,
+                 "mxfp4_quant_1x32: x must be 16-byte and codes 4-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  const int64_t chunks = (int64_t)M * (K / 8);
+  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3(grid_for(chunks, 256)), dim3(256), 0,
+                     as_stream(stream), x, M, K, ldx, row_gather, row_count, codes, scales);
+  return check_launch("mxfp4_quant_1x32");
+}
+
+extern "C" size_t nvfp4_qdq_workspace(void) { return 256; }
+
+extern "C" int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
+                         const float* tensor_scale_in, uint16_t* y, uint8_t* codes,
+                         uint8_t* scales_e4m3, float* tensor_scale_out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  FP4MOE_REQUIRE(M >= 0 && K > 0 && K % 16 == 0, "nvfp4_qdq: M=%d K=%d (K %% 16 != 0)", M, K);
+  if (M == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(x && y, "nvfp4_qdq: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)y & 15) == 0 &&
+                     ((uintptr_t)codes & 3) == 0,
+                 "nvfp4_qdq: x, y must be 16-byte and codes 4-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  hipStream_t s = as_stream(stream);
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  const int64_t chunks = (int64_t)M * (K / 8);
+  if (!tensor_scale_in) {
+    if (!workspace || workspace_bytes < nvfp4_qdq_workspace())
+      return set_error(FP4MOE_ERR_WORKSPACE, "nvfp4_qdq: dynamic scale needs %zu bytes",
+                       nvfp4_qdq_workspace());
+    hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, s, ws);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid_for(chunks, 256 * 8)), dim3(256), 0, s, x, M,
+                       K, row_count, ws);
+  }
+  hipLaunchKernelGGL(nvfp4_qdq_kernel, dim3(grid_for(chunks, 256)), dim3(256), 0, s, x, M, K,
+                     row_count, tensor_scale_in, ws, y, codes, scales_e4m3, tensor_scale_out);
+  return check_launch("nvfp4_qdq");
+}

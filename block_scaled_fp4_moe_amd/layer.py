@@ -1,0 +1,130 @@
+"""The MoE layer as a chain of the C-ABI calls (marshalling and buffer reuse only).
+
+Order ([ATOM] "Stage D: MXFP4 Fused MoE", [NVFP4] "Weight Dequantization and
+Activation QDQ"): moe_route -> moe_permute -> activation quantization
+(mxfp4_quant_1x32 | nvfp4_qdq | none) -> fp4_grouped_gemm stage 1 (gate/up,
+SiLU*up) -> quantization of h -> fp4_grouped_gemm stage 2 (down) ->
+moe_combine.  Every step is a kernel of libfp4moe; this module only
+allocates device buffers (once per token count) and passes pointers.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (A_BF16, A_MXFP4, WFMT, fp4_grouped_gemm, moe_combine, moe_permute,
+               moe_permute_max_tiles, moe_route, mxfp4_quant_1x32, nvfp4_qdq, load)
+
+
+@dataclass
+class LayerConfig:
+    H: int
+    I: int
+    E: int                 # routed experts
+    n_shared: int          # shared experts (ids E .. E+n_shared-1 in the weight tensors)
+    n_group: int
+    topk_group: int
+    topk: int
+    afmt: str              # bf16 | mx | nvfp4
+    wfmt: str              # mx | nvfp4 | fp8
+    block_m: int = 16
+    renormalize: bool = True
+    routed_scale: float = 1.0
+
+
+class MoELayer:
+    """Weights (device tensors):
+         w13 [E+n_shared, 2I, H/2] (FP8: [.., H]), w13_scale (E8M0 [.., H/32] |
+         E4M3 [.., H/16] | float32 channel scale [E+n_shared, 2I]), w13_ts float32
+         [E+n_shared] for NVFP4; w2 / w2_scale / w2_ts likewise with [H, I]."""
+
+    def __init__(self, cfg: LayerConfig, weights: dict, device="cuda"):
+        load()
+        self.cfg = cfg
+        self.w = weights
+        self.device = device
+        self._bufs = {}
+        self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
+
+    def _buffers(self, T):
+        if T in self._bufs:
+            return self._bufs[T]
+        c = self.cfg
+        k = c.topk + c.n_shared
+        P = T * k
+        dev = self.device
+        mt = moe_permute_max_tiles(T, c.topk, c.E, c.n_shared, c.block_m)
+        b = dict(
+            topk_ids=torch.empty((T, c.topk), dtype=torch.int32, device=dev),
+            topk_w=torch.empty((T, c.topk), dtype=torch.float32, device=dev),
+            perm=dict(expert_offsets=torch.empty(c.E + c.n_shared + 1, dtype=torch.int32, device=dev),
+                      sorted_pairs=torch.empty(P, dtype=torch.int32, device=dev),
+                      pair_pos=torch.empty(P, dtype=torch.int32, device=dev),
+                      tiles=torch.empty((max(mt, 1), 2), dtype=torch.int32, device=dev),
+                      n_tiles=torch.empty(1, dtype=torch.int32, device=dev),
+                      n_dropped=torch.empty(1, dtype=torch.int32, device=dev)),
+            perm_ws=torch.empty(max(1, load().moe_permute_workspace(T, c.topk, c.E, c.n_shared,
+                                                                    c.block_m)),
+                                dtype=torch.uint8, device=dev),
+            h=torch.empty((P, c.I), dtype=torch.bfloat16, device=dev),
+            y=torch.empty((P, c.H), dtype=torch.bfloat16, device=dev),
+            out=torch.empty((T, c.H), dtype=torch.bfloat16, device=dev),
+        )
+        if c.afmt == "mx":
+            b["xq"] = torch.empty((T, c.H // 2), dtype=torch.uint8, device=dev)
+            b["xs"] = torch.empty((T, c.H // 32), dtype=torch.uint8, device=dev)
+            b["hq"] = torch.empty((P, c.I // 2), dtype=torch.uint8, device=dev)
+            b["hs"] = torch.empty((P, c.I // 32), dtype=torch.uint8, device=dev)
+        elif c.afmt == "nvfp4":
+            b["xq"] = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
+            b["hq"] = torch.empty((P, c.I), dtype=torch.bfloat16, device=dev)
+        self._bufs[T] = b
+        return b
+
+    def forward(self, x, logits, bias, keep=False, stream=None):
+        """x bf16 [T, H], logits float32 [T, E], bias float32 [E] -> out bf16 [T, H].
+
+        With keep=True returns the dict of every intermediate buffer."""
+        c = self.cfg
+        T = x.shape[0]
+        k = c.topk + c.n_shared
+        b = self._buffers(T)
+        moe_route(logits, bias, c.n_group, c.topk_group, c.topk, c.renormalize, c.routed_scale,
+                  topk_ids=b["topk_ids"], topk_w=b["topk_w"], stream=stream)
+        perm = moe_permute(b["topk_ids"], c.E, c.n_shared, c.block_m, workspace=b["perm_ws"],
+                           out=b["perm"], stream=stream)
+        n_rows = perm["expert_offsets"][c.E + c.n_shared:]     # device row count
+        wf = WFMT[c.wfmt]
+        w = self.w
+        if c.afmt == "mx":
+            mxfp4_quant_1x32(x, codes=b["xq"], scales=b["xs"], stream=stream)
+            a1, a1s, af = b["xq"], b["xs"], A_MXFP4
+        elif c.afmt == "nvfp4":
+            nvfp4_qdq(x, y=b["xq"], workspace=self.nvfp4_ws, stream=stream)
+            a1, a1s, af = b["xq"], None, A_BF16
+        else:
+            a1, a1s, af = x, None, A_BF16
+        ts13 = w.get("w13_ts") if c.wfmt == "nvfp4" else None
+        cs13 = w["w13_scale"] if c.wfmt == "fp8" else None
+        fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
+                         perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
+                         a_row_gather=perm["sorted_pairs"], gather_div=k, out=b["h"],
+                         stream=stream)
+        if c.afmt == "mx":
+            mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
+                             stream=stream)
+            a2, a2s = b["hq"], b["hs"]
+        elif c.afmt == "nvfp4":
+            nvfp4_qdq(b["h"], row_count=n_rows, y=b["hq"], workspace=self.nvfp4_ws,
+                      stream=stream)
+            a2, a2s = b["hq"], None
+        else:
+            a2, a2s = b["h"], None
+        ts2 = w.get("w2_ts") if c.wfmt == "nvfp4" else None
+        cs2 = w["w2_scale"] if c.wfmt == "fp8" else None
+        fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
+                         c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
+                         out=b["y"], stream=stream)
+        moe_combine(b["y"], perm["pair_pos"], b["topk_w"], c.topk, c.n_shared, out=b["out"],
+                    stream=stream)
+        return b if keep else b["out"]

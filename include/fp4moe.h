@@ -1,0 +1,228 @@
+/*
+ * fp4moe -- routed-expert MoE layer with block-scaled FP4 weights, for AMD
+ * Instinct MI355X (gfx950).  C ABI.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory, keeps no device state and never
+ *     synchronizes: each call enqueues its kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and returns.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid call returns FP4MOE_ERR_INVALID_ARG and launches nothing.
+ *     fp4moe_last_error() then returns a thread-local message.
+ *   - Data-dependent conditions found on the device (ids out of range, NaN
+ *     scales, inexact conversions) are reported through caller-provided
+ *     device counters and status arrays, never by faulting.
+ *   - bf16 tensors are passed as uint16_t bit patterns; FP4 payloads, E8M0,
+ *     E4M3 and FP8 codes as uint8_t.  All matrices are row-major.
+ *   - FP4 payloads pack element 2i in the low nibble and 2i+1 in the high
+ *     nibble of byte i.  E2M1 magnitudes are {0, .5, 1, 1.5, 2, 3, 4, 6},
+ *     bit 3 is the sign.  An E8M0 byte c scales by 2^(c-127); 255 is NaN.
+ *     FP8 is OCP E4M3FN (bias 7, max 448, 0x7F/0xFF NaN).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [ATOM]  "Serve Kimi-K2.5-MXFP4 on MI355X with ATOM"
+ *   [NVFP4] "Serving NVFP4 models on AMD Instinct MI355 accelerators"
+ *   [GAUDI] "Kimi-K2.7-Code on Gaudi 2"
+ *   [K3]    "Kimi K3 on MI355X"
+ */
+#ifndef FP4MOE_H
+#define FP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FP4MOE_OK = 0,
+  FP4MOE_ERR_INVALID_ARG = 1,  /* bad shape, null pointer, unsupported combination   */
+  FP4MOE_ERR_UNSUPPORTED = 2,  /* device is not gfx950                                */
+  FP4MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the *_workspace size */
+  FP4MOE_ERR_LAUNCH = 4        /* the HIP runtime reported an error at launch          */
+};
+
+/* Weight formats of fp4_grouped_gemm. */
+enum {
+  FP4MOE_W_MXFP4 = 0,  /* E2M1 codes [E,N,K/2] + E8M0 scales [E,N,K/32]                     */
+  FP4MOE_W_NVFP4 = 1,  /* E2M1 codes [E,N,K/2] + E4M3 scales [E,N,K/16] + fp32 tensor scale [E] */
+  FP4MOE_W_FP8 = 2     /* E4M3 codes [E,N,K] + fp32 per-row channel scale [E,N]              */
+};
+
+/* Activation formats of fp4_grouped_gemm. */
+enum {
+  FP4MOE_A_BF16 = 0,   /* bf16 [rows, K]: weights are decoded to bf16 inside the GEMM tile  */
+  FP4MOE_A_MXFP4 = 1   /* E2M1 codes [rows, K/2] + E8M0 [rows, K/32]: gfx950 scaled MFMA    */
+};
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* fp4moe_last_error(void);
+
+/* Checks that the current HIP device is gfx950.  Returns FP4MOE_OK or
+ * FP4MOE_ERR_UNSUPPORTED.  Every other entry point performs the same check
+ * once per device. */
+int fp4moe_init(void);
+
+/*
+ * moe_route -- grouped sigmoid top-k routing with a correction bias.
+ * [GAUDI] "What was built": the grouped top-k router with sigmoid scoring and
+ * a correction bias; introduction: DeepSeek-V3-style tower, 384 routed experts.
+ * Per token t (float32 decisions, identical to the oracle's reading):
+ *   s_e   = float32(1/(1+exp(-logit)))  evaluated in float64, rounded once
+ *   key_e = float32(s_e + bias_e)
+ *   n_group > 1: groups of E/n_group contiguous experts, group score =
+ *   float32(top1 key + top2 key); the topk_group best groups are kept (ties:
+ *   lower group index).  Then the topk best keys among kept experts in
+ *   descending order (ties: lower id) give topk_ids[t, 0..topk-1].
+ *   topk_w[t,j] = s_j / sum(s_selected) (if renormalize) * routed_scale.
+ * logits float32 [T,E], bias float32 [E] (NULL = zeros) -> topk_ids int32
+ * [T,topk], topk_w float32 [T,topk].
+ * Requires 1 <= E <= 1024, E % n_group == 0, E/n_group >= 2 when n_group > 1,
+ * 1 <= topk_group <= n_group, 1 <= topk <= topk_group*E/n_group, topk <= 32.
+ */
+int moe_route(const float* logits, const float* bias, int T, int E, int n_group,
+              int topk_group, int topk, int renormalize, float routed_scale,
+              int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_permute -- stable sort of the T*k (token, slot) pairs by expert.
+ * [NVFP4] "Memory Management": only dispatched experts are touched;
+ * [GAUDI] "What it taught about Gaudi": cost follows the routing, empty expert
+ * slots are skipped; [K3]: expert tiles carry padding.
+ * k = topk + n_shared; pair p = t*k + j; slot j >= topk is shared expert
+ * E + (j - topk).  Ids outside [0,E) are dropped (pair_pos = -1, counted in
+ * n_dropped).  Kept pairs are sorted by expert, ascending p within an expert.
+ * Outputs (device):
+ *   expert_offsets int32 [E+n_shared+1]  exclusive prefix sum of the counts
+ *   sorted_pairs   int32 [T*k]           pair at each sorted position, -1 past the end
+ *   pair_pos       int32 [T*k]           sorted position of each pair, -1 if dropped
+ *   tiles          int32 [max_tiles, 2]  (expert, m_tile) for every block_m rows
+ *                                         of every non-empty expert, in expert order
+ *   n_tiles        int32 [1]
+ *   n_dropped      int32 [1]
+ * max_tiles = moe_permute_max_tiles(...).  The workspace (device, size from
+ * moe_permute_workspace, may be 0 bytes for small T) holds per-block counts.
+ * Requires T >= 0, 1 <= topk <= 32, 0 <= n_shared <= 8, 1 <= E+n_shared <= 4096,
+ * 1 <= block_m <= 1024.
+ */
+int moe_permute_max_tiles(int T, int topk, int E, int n_shared, int block_m);
+size_t moe_permute_workspace(int T, int topk, int E, int n_shared, int block_m);
+int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int n_shared, int block_m,
+                void* workspace, size_t workspace_bytes, int32_t* expert_offsets,
+                int32_t* sorted_pairs, int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles,
+                int32_t* n_dropped, void* stream);
+
+/*
+ * mxfp4_quant_1x32 -- dynamic 1x32 MXFP4 quantization of bf16 rows.
+ * [ATOM] "Stage B: Dynamic Activation Quantization": live bf16 activations
+ * become FP4 payloads plus E8M0 scales, one per 32 values along K.
+ * Per 32-block: e = floor(log2 amax) - 2 clamped to [-127,127] (amax = 0 gives
+ * -127), scale byte e+127; code = E2M1 nearest to x/2^e, ties to even,
+ * saturating at +-6, sign kept.
+ * x bf16 with row stride ldx (elements); output row r reads input row
+ * row_gather[r] when row_gather != NULL.  row_count (device, NULL = M) limits
+ * the rows processed; rows at or past it are not written.
+ * -> codes uint8 [M, K/2], scales uint8 [M, K/32].  K % 32 == 0.
+ */
+int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx, const int32_t* row_gather,
+                     const int32_t* row_count, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * nvfp4_qdq -- NVFP4 quantize-dequantize round trip of bf16 activations.
+ * [NVFP4] "Weight Dequantization and Activation QDQ".  IEEE float32 steps:
+ *   s_t = tensor_scale_in ? *tensor_scale_in : amax(|x|)/2688 (1 if amax = 0)
+ *   per 16-block: sb = E4M3_RNE_sat(amax_b / f32(6*s_t));
+ *   code = E2M1_RNE_sat(x / f32(sb*s_t)) (all zero when sb = 0, sign kept);
+ *   y = bf16(f32(q*sb) * s_t).
+ * x, y bf16 [M,K] (K % 16 == 0); codes [M,K/2], scales_e4m3 [M,K/16] and
+ * tensor_scale_out [1] are optional (NULL).  row_count as in mxfp4_quant_1x32.
+ * The dynamic scale needs a workspace of nvfp4_qdq_workspace() bytes.
+ */
+size_t nvfp4_qdq_workspace(void);
+int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
+              const float* tensor_scale_in, uint16_t* y, uint8_t* codes, uint8_t* scales_e4m3,
+              float* tensor_scale_out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp4_grouped_gemm -- one GEMM stage over all expert segments.
+ * [ATOM] "Stage D: MXFP4 Fused MoE" (stage 1 on fused gate/up weights, stage
+ * 2 on down weights) and "When Is the Scale Applied?" (scale before the MFMA
+ * for the bf16 path, inside the scaled MFMA for FP4 x FP4); [NVFP4] "Memory
+ * Management" (MoE path: dequantization fused into the GEMM tile, no bf16
+ * weight buffer); [GAUDI] "What was built" (gate and up rows concatenated).
+ *   stage 1: per row r of expert e: [g | u] = A[r] . W_e^T (N = 2I, gate rows
+ *            first); out[r, n] = bf16(SiLU(g_n) * u_n), n < I.
+ *   stage 2: out[r, n] = bf16(A[r] . W_e^T), n < N.
+ * Rows are the sorted pairs: expert e owns rows expert_offsets[e] ..
+ * expert_offsets[e+1]-1; the tile list comes from moe_permute with the same
+ * block_m.  A row r is read from A row a_row_gather[r] / gather_div when
+ * a_row_gather != NULL (stage 1 passes sorted_pairs and k), else row r.
+ * Supported (wfmt, afmt): (MXFP4, BF16), (NVFP4, BF16), (MXFP4, MXFP4),
+ * (FP8, MXFP4).  K % 128 == 0, N % 32 == 0 (stage 1: N % 64 == 0);
+ * block_m in {16, 32, 64} for afmt BF16 and {32, 64, 128, 256} for MXFP4.
+ */
+typedef struct {
+  int stage;               /* 1 or 2                                                */
+  int wfmt;                /* FP4MOE_W_*                                            */
+  int afmt;                /* FP4MOE_A_*                                            */
+  int n_experts;           /* experts in the weight tensors (routed + shared)      */
+  int N;                   /* weight rows per expert (stage 1: 2I)                 */
+  int K;                   /* reduction length                                     */
+  int max_rows;            /* rows of the sorted A / out buffers                   */
+  int max_tiles;           /* rows of `tiles` (moe_permute_max_tiles)               */
+  int block_m;             /* rows per tile                                        */
+  int gather_div;          /* divisor applied to a_row_gather entries (>= 1)        */
+  const uint8_t* w;        /* weight codes                                         */
+  const uint8_t* w_scale;  /* E8M0 [E,N,K/32] | E4M3 [E,N,K/16] | unused (FP8)     */
+  const float* w_tensor_scale;   /* NVFP4: [E]; else NULL                          */
+  const float* w_channel_scale;  /* FP8: [E,N]; else NULL                          */
+  const void* a;           /* bf16 [.,lda] or E2M1 codes [., lda/2]                */
+  const uint8_t* a_scale;  /* MXFP4 activations: E8M0 [., K/32]                    */
+  int64_t lda;             /* A row stride in ELEMENTS                             */
+  const int32_t* a_row_gather;
+  const int32_t* expert_offsets;
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  uint16_t* out;           /* bf16 [max_rows, ldo]                                 */
+  int64_t ldo;             /* out row stride in elements                           */
+  float* out_f32;          /* optional float32 copy before bf16 rounding, stride ldo */
+} fp4moe_gemm_args;
+
+int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);
+
+/*
+ * moe_combine -- weighted top-k combine.
+ * [ATOM] "Stage D: MXFP4 Fused MoE" (stage-2 outputs reduced per token);
+ * [K3]: the shared-expert contribution is added to the routed sum.
+ * out[t] = bf16( sum_{j<topk} w[t,j] * y[pair_pos[t*k+j]]
+ *              + sum_{i<n_shared} y[pair_pos[t*k+topk+i]] ), float32, j ascending;
+ * pairs with pair_pos = -1 contribute nothing.  y bf16 [rows, H] (sorted
+ * order); out bf16 [T,H]; out_f32 optional.  H % 8 == 0.
+ */
+int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w, int T,
+                int topk, int n_shared, int H, uint16_t* out, float* out_f32, void* stream);
+
+/*
+ * mxfp4_to_fp8_channel -- exact MXFP4 -> FP8 E4M3 per-channel conversion.
+ * [GAUDI] "Exact MXFP4 to FP8 per-channel conversion": per row, k = (exponent
+ * of the row's largest element) - 7, each element becomes the E4M3 code of
+ * x/2^k, channel_scale = 2^k.  Exact when the row's E8M0 scales span <= 9 binades.
+ * row_status (optional): 0 exact, every element exponent in [-5,7];
+ * 1 an element falls below the -5 floor; 2 a block has E8M0 255 (its codes
+ * become 0x7F, k from the finite blocks); 3 the finite part of the row is
+ * zero (k = 0).  n_inexact_rows (device, required) receives the number of
+ * rows where some finite element is not reproduced exactly; the call sets it.
+ * codes [rows, K/2], scales [rows, K/32] -> fp8 [rows, K], channel_scale
+ * float32 [rows].  K % 32 == 0.
+ */
+int mxfp4_to_fp8_channel(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
+                         uint8_t* fp8, float* channel_scale, uint8_t* row_status,
+                         uint32_t* n_inexact_rows, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4MOE_H */

@@ -1,0 +1,94 @@
+"""The C-ABI library loads on the host, exports every declared symbol, and its
+host-side logic (argument validation, size queries) behaves as documented.
+No GPU is needed: every call here returns before any device work."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_moe_amd as fm
+from oracle import permute as OP
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fp4moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fm.load()
+    names = declared_functions()
+    assert len(names) == 12, names
+    for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
+              "moe_combine", "mxfp4_to_fp8_channel"]:
+        assert n in names
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_permute_size_queries_match_oracle_bound():
+    lib = fm.load()
+    for T, topk, E, ns, bm in [(1, 8, 384, 1, 16), (64, 8, 384, 1, 16), (8192, 8, 384, 1, 256),
+                               (16, 2, 8, 0, 16), (0, 8, 384, 1, 16), (5, 1, 8, 0, 4)]:
+        assert lib.moe_permute_max_tiles(T, topk, E, ns, bm) == OP.max_tiles(T, topk, E, ns, bm)
+    assert lib.moe_permute_workspace(64, 8, 384, 1, 16) == 0          # single-wave path
+    assert lib.moe_permute_workspace(8192, 8, 384, 1, 256) == 72 * 385 * 4
+
+
+def _status(call):
+    lib = fm.load()
+    st = call(lib)
+    return st, lib.fp4moe_last_error().decode()
+
+
+@pytest.mark.parametrize("bad", [
+    dict(E=0), dict(E=2000), dict(n_group=5), dict(topk_group=9), dict(topk=0), dict(topk=33),
+    dict(n_group=384, topk_group=1)])
+def test_route_rejects_bad_arguments(bad):
+    a = dict(T=4, E=384, n_group=8, topk_group=4, topk=8)
+    a.update(bad)
+    st, msg = _status(lambda lib: lib.moe_route(None, None, a["T"], a["E"], a["n_group"],
+                                                 a["topk_group"], a["topk"], 1, 1.0, None, None,
+                                                 None))
+    assert st == 1 and "moe_route" in msg
+
+
+def test_quant_and_convert_reject_bad_K():
+    st, msg = _status(lambda lib: lib.mxfp4_quant_1x32(None, 4, 48, 48, None, None, None, None,
+                                                        None))
+    assert st == 1 and "K" in msg
+    st, msg = _status(lambda lib: lib.nvfp4_qdq(None, 4, 24, None, None, None, None, None, None,
+                                                 None, 0, None))
+    assert st == 1
+    st, msg = _status(lambda lib: lib.mxfp4_to_fp8_channel(None, None, 4, 40, None, None, None,
+                                                            None, None))
+    assert st == 1
+    st, msg = _status(lambda lib: lib.moe_combine(None, None, None, 2, 8, 1, 7164, None, None,
+                                                   None))
+    assert st == 1
+
+
+def test_gemm_rejects_unsupported_combinations():
+    def run(**kw):
+        a = dict(stage=1, wfmt=0, afmt=0, n_experts=4, N=256, K=256, max_rows=8, max_tiles=4,
+                 block_m=16, gather_div=1, lda=256, ldo=128)
+        a.update(kw)
+        args = fm.GemmArgs(a["stage"], a["wfmt"], a["afmt"], a["n_experts"], a["N"], a["K"],
+                           a["max_rows"], a["max_tiles"], a["block_m"], a["gather_div"],
+                           None, None, None, None, None, None, a["lda"], None, None, None, None,
+                           None, a["ldo"], None)
+        return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
+    assert run(stage=3)[0] == 1
+    assert run(wfmt=2, afmt=0)[0] == 1          # FP8 weights need MXFP4 activations
+    assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
+    assert run(K=96)[0] == 1
+    assert run(block_m=128)[0] == 1             # bf16 path tiles are 16/32/64 rows
+    assert run(afmt=1, block_m=16)[0] == 1
+    assert run(N=96)[0] == 1
+    assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers

@@ -1,0 +1,175 @@
+"""GPU parity of fp4_grouped_gemm (both stages, every supported format pair).
+
+Each stage is checked on its own synthetic inputs (stage 2 gets a synthetic h,
+never the GPU's stage-1 output), so the expected values come from the oracle
+alone.  Shapes span several tiles per expert with ragged tails, a shared
+expert, empty experts, and the full 7168/2048 layer width.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import gemm as OG
+from oracle import permute as OP
+from oracle import quant as OQ
+
+from .parity import assert_bf16_close, assert_float_close
+from .test_gpu_kernels import bf16_dev, bits_of, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def make_weights(rng, Et, N, K, wfmt, lo=-6, hi=0):
+    """Synthetic weights of one projection: dict(codes, scale[, ts]) as numpy."""
+    if wfmt == "mx":
+        return dict(codes=rng.integers(0, 256, (Et, N, K // 2), dtype=np.uint8),
+                    scale=(127 + rng.integers(lo, hi + 1, (Et, N, K // 32))).astype(np.uint8))
+    if wfmt == "nvfp4":
+        return dict(codes=rng.integers(0, 256, (Et, N, K // 2), dtype=np.uint8),
+                    scale=synth.e4m3_from_f32(np.abs(rng.standard_normal((Et, N, K // 16),
+                                                                         dtype=np.float32))),
+                    ts=rng.uniform(0.01, 0.02, Et).astype(np.float32))
+    if wfmt == "fp8":
+        c = rng.integers(0, 256, (Et, N, K), dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x3C
+        return dict(codes=c, scale=np.ldexp(1.0, rng.integers(-9, -3, (Et, N))).astype(np.float32))
+    raise ValueError(wfmt)
+
+
+def oracle_weight(wd, wfmt, e):
+    if wfmt == "nvfp4":
+        return OG.dequant_expert(wfmt, wd["codes"][e], wd["scale"][e], wd["ts"][e])
+    return OG.dequant_expert(wfmt, wd["codes"][e], wd["scale"][e])
+
+
+def gpu_weight_args(wd, wfmt):
+    kw = dict(w=dev(wd["codes"]))
+    if wfmt == "fp8":
+        kw.update(w_scale=None, w_channel_scale=dev(wd["scale"]))
+    else:
+        kw.update(w_scale=dev(wd["scale"]))
+    if wfmt == "nvfp4":
+        kw.update(w_tensor_scale=dev(wd["ts"]))
+    return kw
+
+
+def routing(rng, T, topk, E, skew=False):
+    if skew:
+        p = 1.0 / np.arange(1, E + 1) ** 1.5
+        p /= p.sum()
+        return np.stack([rng.choice(E, topk, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    return np.stack([rng.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+
+
+def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
+              exact=False):
+    rng = np.random.default_rng(seed)
+    Et = E + ns
+    k = topk + ns
+    ids = routing(rng, T, topk, E, skew)
+    perm_ref = OP.moe_permute(ids, E, ns, bm)
+    perm = gpu_lib.moe_permute(dev(ids), E, ns, bm)
+    n_rows = int(perm_ref["expert_offsets"][-1])
+    N, K = (2 * I, H) if stage == 1 else (H, I)
+    if exact:
+        wd = dict(codes=rng.integers(0, 256, (Et, N, K // 2), dtype=np.uint8),
+                  scale=np.full((Et, N, K // 32), 127, np.uint8))
+        vals = np.array([0, .5, 1, 1.5, 2, -.5, -1, -1.5, -2], np.float32)
+    else:
+        wd = make_weights(rng, Et, N, K, wfmt)
+    # activations: stage 1 reads token rows through the gather, stage 2 sorted rows
+    rows_in = T if stage == 1 else T * k
+    if exact:
+        xf = vals[rng.integers(0, len(vals), (rows_in, K))]
+    else:
+        xf = rng.standard_normal((rows_in, K), dtype=np.float32) * np.float32(1 if stage == 1 else 20)
+    xb = synth.bf16_from_f32(xf)
+    poison = stage == 2 and n_rows < rows_in     # rows past the valid count are never read
+    if afmt == "mx":
+        qc, qs = OQ.mxfp4_quant_1x32(xb)
+        a_vals = F.mxfp4_dequant(qc, qs)
+        if poison:
+            qs = qs.copy()
+            qs[n_rows:] = 255
+        a_kw = dict(a=dev(qc), a_scale=dev(qs), afmt=gpu_lib.A_MXFP4)
+    else:
+        a_vals = F.bf16_decode(xb)
+        if poison:
+            xb = xb.copy()
+            xb[n_rows:] = 0x7FC0
+        a_kw = dict(a=bf16_dev(xb), afmt=gpu_lib.A_BF16)
+    if stage == 1:
+        a_sorted = a_vals[perm_ref["sorted_pairs"][:n_rows] // k]
+        gather = dict(a_row_gather=perm["sorted_pairs"], gather_div=k)
+    else:
+        a_sorted = a_vals[:n_rows]
+        gather = {}
+    n_out = N // 2 if stage == 1 else N
+    out_f32 = torch.full((T * k, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    afmt_code = a_kw.pop("afmt")
+    out = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.WFMT[wfmt], afmt_code,
+                                   perm=perm, block_m=bm, out_f32=out_f32,
+                                   **gpu_weight_args(wd, wfmt), **a_kw, **gather)
+    ref_unrounded = OG.grouped_stage(stage, a_sorted, perm_ref["expert_offsets"],
+                                     lambda e: oracle_weight(wd, wfmt, e), rounding=False)
+    g_bits = bits_of(out)[:n_rows]
+    g_f32 = host(out_f32)[:n_rows]
+    if exact:
+        assert np.array_equal(g_f32.astype(np.float64), ref_unrounded), "exact special case"
+        return
+    assert_float_close(g_f32, ref_unrounded, f"stage{stage} {wfmt}/{afmt} f32")
+    assert_bf16_close(g_bits, ref_unrounded, f"stage{stage} {wfmt}/{afmt} bf16")
+
+
+DQ_CASES = [
+    # stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew
+    (1, "mx", 16, 2, 8, 0, 256, 128, 16, 1, False),
+    (2, "mx", 16, 2, 8, 0, 256, 128, 16, 2, False),
+    (1, "mx", 70, 3, 6, 1, 512, 256, 16, 3, True),
+    (2, "mx", 70, 3, 6, 1, 512, 256, 16, 4, True),
+    (1, "mx", 90, 4, 10, 1, 1024, 256, 32, 5, True),
+    (2, "mx", 90, 4, 10, 1, 1024, 256, 64, 6, True),
+    (1, "mx", 3, 2, 4, 1, 7168, 2048, 16, 7, False),
+    (2, "mx", 3, 2, 4, 1, 7168, 2048, 16, 8, False),
+    (1, "nvfp4", 60, 4, 8, 0, 512, 256, 64, 9, True),
+    (2, "nvfp4", 60, 4, 8, 0, 512, 256, 64, 10, True),
+    (1, "nvfp4", 40, 2, 12, 0, 1024, 512, 16, 11, False),
+]
+
+
+@pytest.mark.parametrize("case", DQ_CASES)
+def test_dq_gemm_parity(gpu_lib, case):
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "bf16", T, topk, E, ns, H, I, bm, seed, skew)
+
+
+MX_CASES = [
+    (1, "mx", 16, 2, 8, 0, 256, 128, 32, 21, False),
+    (2, "mx", 16, 2, 8, 0, 256, 128, 32, 22, False),
+    (1, "mx", 200, 3, 6, 1, 512, 256, 64, 23, True),
+    (2, "mx", 200, 3, 6, 1, 512, 256, 64, 24, True),
+    (1, "mx", 400, 4, 8, 1, 512, 256, 128, 25, True),
+    (2, "mx", 400, 4, 8, 1, 512, 256, 256, 26, True),
+    (1, "mx", 5, 2, 4, 1, 7168, 2048, 32, 27, False),
+    (2, "mx", 5, 2, 4, 1, 7168, 2048, 32, 28, False),
+    (1, "fp8", 150, 3, 6, 1, 512, 256, 64, 29, True),
+    (2, "fp8", 150, 3, 6, 1, 512, 256, 128, 30, True),
+]
+
+
+@pytest.mark.parametrize("case", MX_CASES)
+def test_mx_gemm_parity(gpu_lib, case):
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew)
+
+
+@pytest.mark.parametrize("afmt,bm", [("bf16", 16), ("bf16", 64), ("mx", 64), ("mx", 256)])
+def test_gemm_exact_special_case(gpu_lib, afmt, bm):
+    """E8M0 = 127 weights and activations in {0, +-.5, +-1, +-1.5, +-2}: every
+    product is a multiple of 0.25 below 12, every partial sum of K <= 4096 terms
+    stays below 2^22 in quarter units, so the float32 stage-2 result is exact in
+    any summation order and must equal the oracle bit for bit."""
+    run_stage(gpu_lib, 2, "mx", afmt, 40, 2, 6, 1, 512, 2048, bm, 31, exact=True)

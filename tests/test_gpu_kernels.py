@@ -1,0 +1,254 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle.
+
+Integer / code outputs must match bit for bit; float outputs follow the
+tolerances in tests/parity.py.  Inputs come from seeded generators (synth)
+or are built by hand for edge cases; expected values come from oracle/ only.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import convert as OC
+from oracle import formats as F
+from oracle import gemm as OG
+from oracle import permute as OP
+from oracle import quant as OQ
+from oracle import route as OR
+
+from .parity import assert_bf16_close, assert_equal, assert_float_close
+from .test_oracle_convert import load_convert_golden
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bf16_dev(bits):
+    return dev(np.asarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+
+
+def bits_of(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+# ------------------------------------------------------------------ routing
+
+ROUTE_CASES = [
+    # (T, E, n_group, topk_group, topk, bias_std, seed)
+    (16, 8, 1, 1, 2, 0.1, 1),
+    (64, 384, 8, 4, 8, 0.1, 2),
+    (777, 384, 8, 4, 8, 0.1, 3),
+    (33, 256, 8, 4, 8, 0.0, 4),
+    (5, 1024, 16, 2, 32, 0.5, 5),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES)
+def test_route_parity(gpu_lib, case):
+    T, E, ng, tg, k, bstd, seed = case
+    g = np.random.default_rng(seed)
+    logits = g.standard_normal((T, E), dtype=np.float32)
+    bias = (g.standard_normal(E, dtype=np.float32) * np.float32(bstd)).astype(np.float32)
+    ids, w = gpu_lib.moe_route(dev(logits), dev(bias), ng, tg, k)
+    rid, rw = OR.moe_route(logits, bias, ng, tg, k)
+    assert_equal(host(ids), rid, "topk_ids")
+    np.testing.assert_allclose(host(w), rw, rtol=1e-6, atol=0)
+
+
+def test_route_ties_and_options(gpu_lib):
+    T, E = 3, 384
+    logits = np.zeros((T, E), dtype=np.float32)
+    logits[1, 100:110] = 1.0             # ties inside one group
+    logits[2, ::7] = -1.0
+    bias = np.zeros(E, dtype=np.float32)
+    for renorm, scale in ((True, 1.0), (False, 2.5)):
+        ids, w = gpu_lib.moe_route(dev(logits), dev(bias), 8, 4, 8, renorm, scale)
+        rid, rw = OR.moe_route(logits, bias, 8, 4, 8, renorm, scale)
+        assert_equal(host(ids), rid, "topk_ids ties")
+        np.testing.assert_allclose(host(w), rw, rtol=1e-6)
+    assert list(rid[0]) == list(range(8))
+
+
+def test_route_decode_workload(gpu_lib):
+    w = synth.WORKLOADS["decode"]
+    for T in (1, 8, 64):
+        logits = synth.router_logits(w, T)
+        bias = synth.router_bias(w)
+        ids, wt = gpu_lib.moe_route(dev(logits), dev(bias), w.n_group, w.topk_group, w.topk)
+        rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+        assert_equal(host(ids), rid, f"decode T={T}")
+        np.testing.assert_allclose(host(wt), rw, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ permute
+
+def _perm_check(gpu_lib, ids, E, n_shared, bm):
+    out = gpu_lib.moe_permute(dev(ids), E, n_shared, bm)
+    ref = OP.moe_permute(ids, E, n_shared, bm)
+    assert_equal(host(out["expert_offsets"]), ref["expert_offsets"], "expert_offsets")
+    assert_equal(host(out["sorted_pairs"]), ref["sorted_pairs"], "sorted_pairs")
+    assert_equal(host(out["pair_pos"]), ref["pair_pos"], "pair_pos")
+    nt = int(host(out["n_tiles"])[0])
+    assert nt == ref["n_tiles"]
+    assert_equal(host(out["tiles"])[:nt], ref["tiles"], "tiles")
+    assert int(host(out["n_dropped"])[0]) == ref["n_dropped"]
+
+
+@pytest.mark.parametrize("T,topk,E,ns,bm,seed", [
+    (1, 8, 384, 1, 16, 1), (8, 8, 384, 1, 16, 2), (64, 8, 384, 1, 16, 3),
+    (113, 8, 384, 1, 16, 4),            # 1017 pairs: single-wave path
+    (114, 8, 384, 1, 16, 5),            # 1026 pairs: three-kernel path
+    (3000, 8, 384, 1, 64, 6), (2048, 8, 384, 0, 256, 7), (16, 2, 8, 0, 16, 8),
+    (500, 4, 4000, 2, 32, 9)])
+def test_permute_parity(gpu_lib, T, topk, E, ns, bm, seed):
+    g = np.random.default_rng(seed)
+    ids = np.stack([g.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    _perm_check(gpu_lib, ids, E, ns, bm)
+
+
+def test_permute_dropped_and_skewed(gpu_lib):
+    g = np.random.default_rng(11)
+    for T in (50, 400):
+        ids = g.integers(-3, 390, size=(T, 8)).astype(np.int32)   # duplicates and invalid ids
+        _perm_check(gpu_lib, ids, 384, 1, 16)
+        ids = np.zeros((T, 8), dtype=np.int32)                     # everything on expert 0
+        _perm_check(gpu_lib, ids, 384, 1, 16)
+
+
+def test_permute_empty(gpu_lib):
+    out = gpu_lib.moe_permute(torch.zeros((0, 8), dtype=torch.int32, device="cuda"), 384, 1, 16)
+    assert int(host(out["n_tiles"])[0]) == 0
+    assert np.all(host(out["expert_offsets"]) == 0)
+
+
+# ------------------------------------------------------------------ MXFP4 quant
+
+def _quant_inputs(seed, M, K):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((M, K)).astype(np.float32) * np.exp(g.uniform(-8, 8, (M, 1))).astype(np.float32)
+    xb = synth.bf16_from_f32(x)
+    # edge rows: zeros, -0, bf16 subnormals, largest finite, exact E2M1 tie points
+    xb[0, :] = 0
+    xb[1, :32] = 0x8000
+    xb[2, :] = np.arange(K, dtype=np.uint16) % 128 + 1            # subnormal bf16
+    xb[3, :32] = 0x7f7f                                          # largest finite bf16
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 7.0, 7.5, -0.25, -5.0], np.float32)
+    xb[4, :12] = synth.bf16_from_f32(ties)
+    xb[4, 12:32] = synth.bf16_from_f32(np.full(20, 0.1, np.float32))
+    return xb
+
+
+@pytest.mark.parametrize("M,K", [(16, 256), (37, 7168), (300, 2048)])
+def test_mxfp4_quant_parity(gpu_lib, M, K):
+    xb = _quant_inputs(M + K, M, K)
+    codes, scales = gpu_lib.mxfp4_quant_1x32(bf16_dev(xb))
+    rc, rs = OQ.mxfp4_quant_1x32(xb)
+    assert_equal(host(scales), rs, "scales")
+    assert_equal(host(codes), rc, "codes")
+
+
+def test_mxfp4_quant_gather_and_row_count(gpu_lib):
+    xb = _quant_inputs(5, 40, 512)
+    gather = np.random.default_rng(6).integers(0, 40, 70).astype(np.int32)
+    codes = torch.full((70, 256), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((70, 16), 0xCD, dtype=torch.uint8, device="cuda")
+    rc_dev = dev(np.array([51], dtype=np.int32))
+    gpu_lib.mxfp4_quant_1x32(bf16_dev(xb), row_gather=dev(gather), row_count=rc_dev,
+                             codes=codes, scales=scales)
+    rc, rs = OQ.mxfp4_quant_1x32(xb[gather])
+    assert_equal(host(codes)[:51], rc[:51], "gathered codes")
+    assert_equal(host(scales)[:51], rs[:51], "gathered scales")
+    assert np.all(host(codes)[51:] == 0xAB) and np.all(host(scales)[51:] == 0xCD)
+
+
+# ------------------------------------------------------------------ NVFP4 QDQ
+
+@pytest.mark.parametrize("M,K,static", [(16, 256, False), (64, 7168, False), (33, 2048, True)])
+def test_nvfp4_qdq_parity(gpu_lib, M, K, static):
+    g = np.random.default_rng(M * K)
+    xb = synth.bf16_from_f32(g.standard_normal((M, K)).astype(np.float32) *
+                             np.exp(g.uniform(-3, 3, (M, 1))).astype(np.float32))
+    xb[1, :16] = 0
+    ts = np.float32(0.0037) if static else None
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
+    tso = torch.empty(1, dtype=torch.float32, device="cuda")
+    y = gpu_lib.nvfp4_qdq(bf16_dev(xb), tensor_scale=None if ts is None else dev(np.array([ts])),
+                          codes=codes, scales=scales, tensor_scale_out=tso)
+    ref = OQ.nvfp4_qdq(xb, tensor_scale_in=ts)
+    assert host(tso)[0] == np.float32(ref["tensor_scale"])
+    assert_equal(host(scales), ref["scales"], "e4m3 scales")
+    assert_equal(host(codes), ref["codes"], "codes")
+    assert_equal(bits_of(y), ref["y"], "y")
+
+
+def test_nvfp4_qdq_row_count_and_zero(gpu_lib):
+    g = np.random.default_rng(3)
+    xb = synth.bf16_from_f32(g.standard_normal((20, 64)).astype(np.float32))
+    xb[12:] = synth.bf16_from_f32(np.full((8, 64), 1e4, np.float32))   # must not enter amax
+    y = gpu_lib.nvfp4_qdq(bf16_dev(xb), row_count=dev(np.array([12], np.int32)))
+    ref = OQ.nvfp4_qdq(xb[:12])
+    assert_equal(bits_of(y)[:12], ref["y"], "y rows < row_count")
+    y0 = gpu_lib.nvfp4_qdq(bf16_dev(np.zeros((4, 32), np.uint16)))
+    assert np.all(bits_of(y0) == 0)
+
+
+# ------------------------------------------------------------------ FP8 conversion
+
+def _convert_check(gpu_lib, codes, scales):
+    fp8, sc, st, ni = gpu_lib.mxfp4_to_fp8_channel(dev(codes), dev(scales))
+    ref = OC.mxfp4_to_fp8_channel(codes, scales)
+    assert_equal(host(fp8), ref["fp8"], "fp8 codes")
+    assert_equal(host(sc), ref["scale"], "channel scale")
+    assert_equal(host(st), ref["status"], "row status")
+    assert int(host(ni)[0]) == ref["n_inexact"]
+
+
+def test_convert_golden_rows(gpu_lib):
+    cases = load_convert_golden()
+    codes = np.stack([c[1] for c in cases])
+    scales = np.stack([c[2] for c in cases])
+    _convert_check(gpu_lib, codes, scales)
+
+
+@pytest.mark.parametrize("R,K,lo,hi,seed", [(512, 256, 0, 9, 1), (300, 7168, 1, 9, 2),
+                                            (700, 2048, 1, 9, 3), (400, 512, 8, 20, 4),
+                                            (64, 4096, 0, 40, 5)])
+def test_convert_parity(gpu_lib, R, K, lo, hi, seed):
+    g = np.random.default_rng(seed)
+    codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales, _ = synth.spanned_scales(R, K // 32, 5, seed, top_lo=-4, top_hi=0, span_lo=lo,
+                                     span_hi=hi)
+    # sprinkle NaN blocks, zero rows and extreme scale rows
+    scales[3, 1] = 255
+    codes[5] = 0
+    codes[6] = 0x88
+    scales[7] = 254
+    scales[8] = 0
+    _convert_check(gpu_lib, codes, scales)
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("T,topk,ns,H", [(1, 8, 1, 7168), (37, 2, 0, 256), (300, 8, 1, 2048)])
+def test_combine_parity(gpu_lib, T, topk, ns, H):
+    g = np.random.default_rng(T * H)
+    k = topk + ns
+    y = synth.bf16_from_f32(g.standard_normal((T * k, H)).astype(np.float32) * 50)
+    pos = g.permutation(T * k).astype(np.int32)
+    pos[::17] = -1
+    w = g.uniform(0, 1, (T, topk)).astype(np.float32)
+    out_f32 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out = gpu_lib.moe_combine(bf16_dev(y), dev(pos), dev(w), topk, ns, out_f32=out_f32)
+    ref, _ = OG.moe_combine(F.bf16_decode(y), pos, w.astype(np.float64), T, topk, ns)
+    assert_bf16_close(bits_of(out), ref, "combine")
+    assert_float_close(host(out_f32), ref, "combine f32", rel_l2=1e-6, max_abs_rms=1e-5)

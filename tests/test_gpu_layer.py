@@ -1,0 +1,139 @@
+"""End-to-end GPU parity of the whole layer (the seven calls chained) against the
+oracle layer.  Routing ids and permutations bit-exact; the bf16 output within
+the float tolerance of tests/parity.py.
+
+At the full 7168/2048 width only the experts that the (oracle-computed)
+routing selects get weights; every other expert's memory is left
+uninitialized, so reading an expert that received no token would corrupt the
+result.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import convert as OC
+from oracle import layer as OL
+from oracle import route as OR
+
+from .parity import assert_bf16_close, assert_equal
+from .test_gpu_kernels import bf16_dev, bits_of, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def build_weights(w, experts, wfmt, torch_empty_experts):
+    """numpy weights for `experts` (dict e -> arrays) and device tensors with
+    only those experts written."""
+    Et = w.E + w.n_shared
+    H, I = w.H, w.I
+    np_w = {}
+    dev_w = {}
+    if wfmt in ("mx", "fp8"):
+        dev_w["w13"] = torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+        dev_w["w13_scale"] = torch.empty((Et, 2 * I, H // 32), dtype=torch.uint8, device="cuda")
+        dev_w["w2"] = torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda")
+        dev_w["w2_scale"] = torch.empty((Et, H, I // 32), dtype=torch.uint8, device="cuda")
+        if not torch_empty_experts:
+            for t in dev_w.values():
+                t.zero_()
+        np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+        for e in experts:
+            c13, s13 = synth.expert_mx(w, e, 13)
+            c2, s2 = synth.expert_mx(w, e, 2)
+            np_w["w13"][e], np_w["w13_scale"][e] = c13, s13
+            np_w["w2"][e], np_w["w2_scale"][e] = c2, s2
+            dev_w["w13"][e].copy_(torch.from_numpy(c13))
+            dev_w["w13_scale"][e].copy_(torch.from_numpy(s13))
+            dev_w["w2"][e].copy_(torch.from_numpy(c2))
+            dev_w["w2_scale"][e].copy_(torch.from_numpy(s2))
+    elif wfmt == "nvfp4":
+        dev_w["w13"] = torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda")
+        dev_w["w13_scale"] = torch.empty((Et, 2 * I, H // 16), dtype=torch.uint8, device="cuda")
+        dev_w["w2"] = torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda")
+        dev_w["w2_scale"] = torch.empty((Et, H, I // 16), dtype=torch.uint8, device="cuda")
+        ts13 = np.zeros(Et, np.float32)
+        ts2 = np.zeros(Et, np.float32)
+        np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={}, w13_ts=ts13, w2_ts=ts2)
+        for e in experts:
+            c13, s13, t13 = synth.expert_nvfp4(w, e, 13)
+            c2, s2, t2 = synth.expert_nvfp4(w, e, 2)
+            np_w["w13"][e], np_w["w13_scale"][e], ts13[e] = c13, s13, t13
+            np_w["w2"][e], np_w["w2_scale"][e], ts2[e] = c2, s2, t2
+            dev_w["w13"][e].copy_(torch.from_numpy(c13))
+            dev_w["w13_scale"][e].copy_(torch.from_numpy(s13))
+            dev_w["w2"][e].copy_(torch.from_numpy(c2))
+            dev_w["w2_scale"][e].copy_(torch.from_numpy(s2))
+        dev_w["w13_ts"] = dev(ts13)
+        dev_w["w2_ts"] = dev(ts2)
+    if wfmt == "fp8":
+        # FP8 experts are the oracle's exact conversion of the MXFP4 experts
+        f13 = torch.empty((Et, 2 * I, H), dtype=torch.uint8, device="cuda")
+        f2 = torch.empty((Et, H, I), dtype=torch.uint8, device="cuda")
+        cs13 = torch.zeros((Et, 2 * I), dtype=torch.float32, device="cuda")
+        cs2 = torch.zeros((Et, H), dtype=torch.float32, device="cuda")
+        npf = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+        for e in experts:
+            r13 = OC.mxfp4_to_fp8_channel(np_w["w13"][e], np_w["w13_scale"][e])
+            r2 = OC.mxfp4_to_fp8_channel(np_w["w2"][e], np_w["w2_scale"][e])
+            assert r13["n_inexact"] == 0 and r2["n_inexact"] == 0
+            npf["w13"][e], npf["w13_scale"][e] = r13["fp8"], r13["scale"]
+            npf["w2"][e], npf["w2_scale"][e] = r2["fp8"], r2["scale"]
+            f13[e].copy_(torch.from_numpy(r13["fp8"]))
+            f2[e].copy_(torch.from_numpy(r2["fp8"]))
+            cs13[e].copy_(torch.from_numpy(r13["scale"]))
+            cs2[e].copy_(torch.from_numpy(r2["scale"]))
+        np_w = npf
+        dev_w = dict(w13=f13, w13_scale=cs13, w2=f2, w2_scale=cs2)
+    return np_w, dev_w
+
+
+def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, full_width=True):
+    logits = synth.router_logits(w, T, seed)
+    bias = synth.router_bias(w)
+    xb = synth.activations(w, T, seed)
+    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+    experts = sorted(set(rid.reshape(-1).tolist()) | set(range(w.E, w.E + w.n_shared)))
+    np_w, dev_w = build_weights(w, experts, wfmt, torch_empty_experts=True)
+    cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
+                              block_m=block_m)
+    layer = gpu_lib.MoELayer(cfg, dev_w)
+    b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
+    ref = OL.moe_layer(xb, logits, bias, np_w, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                       topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
+                       block_m=block_m, topk_ids=rid, topk_w=rw)
+    assert_equal(host(b["topk_ids"]), rid, "topk_ids")
+    np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
+    assert_equal(host(b["perm"]["sorted_pairs"]), ref["perm"]["sorted_pairs"], "sorted_pairs")
+    assert_equal(host(b["perm"]["pair_pos"]), ref["perm"]["pair_pos"], "pair_pos")
+    n = int(ref["perm"]["expert_offsets"][-1])
+    assert_bf16_close(bits_of(b["h"])[:n], ref["h"], "h")
+    stats = assert_bf16_close(bits_of(b["out"]), ref["out"], "out")
+    return stats
+
+
+def test_layer_tiny_bf16_path(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["tiny"], 16, "bf16", "mx", 16)
+
+
+def test_layer_tiny_mx_path(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["tiny"], 16, "mx", "mx", 32)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_layer_decode_full_width(gpu_lib, T):
+    run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
+
+
+def test_layer_prefill_path_full_width(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", 64)
+
+
+def test_layer_nvfp4_full_width(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", 16)
+
+
+def test_layer_fp8_full_width(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", 32)
