@@ -18,13 +18,21 @@
 // column l % 16 (weight row).
 //
 // Families
-//   dq  (afmt BF16; wfmt MXFP4 | NVFP4): weights decoded to bf16 in registers
-//       (v_cvt_scalef32_pk_*_fp4), v_mfma_f32_16x16x32_bf16.  A workgroup is
-//       four waves that split the K chunks round-robin and reduce through LDS,
-//       so even a single decode token spreads an expert over many CUs.
-//   mx  (afmt MXFP4; wfmt MXFP4 | FP8): v_mfma_scale_f32_16x16x128_f8f6f4 with
-//       the E8M0 bytes as scale operands; FP8 weights carry a per-row float
-//       channel scale applied in the epilogue.
+//   dq  (wfmt MXFP4 | NVFP4 | FP8; afmt BF16, or MXFP4 with FP8 weights):
+//       both operands are brought to bf16 in registers (v_cvt_scalef32_pk_*),
+//       then v_mfma_f32_16x16x32_bf16 with float32 accumulation.  The decode is
+//       exact: E2M1 x E8M0, E2M1 x E4M3 and E4M3 values all fit bf16.  A
+//       workgroup is four waves that split the K chunks round-robin and reduce
+//       through LDS, so even a single decode token spreads an expert over many
+//       CUs.  FP8 weights carry a per-row float channel scale applied in the
+//       epilogue.
+//   mx  (afmt MXFP4; wfmt MXFP4): v_mfma_scale_f32_16x16x128_f8f6f4 FP4 x FP4
+//       with the E8M0 bytes as the scale operands.
+//
+// FP8 weights with MXFP4 activations go through the bf16 path on purpose: in
+// the mixed FP4 x FP8 form of the scaled MFMA each FP4 lane holds halves of
+// two different 32-element K blocks, so one E8M0 scale per lane cannot carry
+// an MX block scale there.  The bf16 path computes the same exact products.
 #include "common.h"
 
 namespace fp4moe {
@@ -100,13 +108,25 @@ __device__ __forceinline__ v8bf decode_nv8(uint32_t d, float scale) {
               nv_pair(d, scale, 3));
 }
 
+// Eight bf16 weights from two dwords of E4M3 codes (exact).
+__device__ __forceinline__ v8bf decode_fp8x8(uint32_t d0, uint32_t d1) {
+  return cat8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
 __device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
 
 // ===========================================================================
 // dq family: bf16 activations, FP4 weights decoded in registers
 // ===========================================================================
 
-template <int WFMT, int STAGE, int MB>
+template <int WFMT, int AFMT, int STAGE, int MB>
 __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
   constexpr int NG = 2;            // two 16-row weight groups per work item
   constexpr int NV = MB * NG * 4;  // accumulator floats per lane
@@ -117,10 +137,9 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
   const int BM = MB * 16;
   const int n_nb = (STAGE == 1) ? (p.N / 2) / 16 : p.N / 32;
   const int nkc = p.K / 128;
-  const int64_t wrow_bytes = p.K / 2;
+  const int64_t wrow_bytes = (WFMT == FP4MOE_W_FP8) ? p.K : p.K / 2;
   const int64_t srow_bytes = (WFMT == FP4MOE_W_MXFP4) ? p.K / 32 : p.K / 16;
   const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
-  const uint16_t* A = static_cast<const uint16_t*>(p.a);
 
   for (int64_t wi = blockIdx.x; wi < n_work; wi += gridDim.x) {
     const int tile = (int)(wi / n_nb), nb = (int)(wi - (int64_t)tile * n_nb);
@@ -130,14 +149,18 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
 
     const uint8_t* wp[NG];
     const uint8_t* sp[NG];
+    int wrow[NG];
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
       const int wr = (STAGE == 1) ? (ng * (p.N / 2) + nb * 16 + r16) : (nb * 32 + ng * 16 + r16);
+      wrow[ng] = wr;
       const int64_t row = (int64_t)e * p.N + wr;
       wp[ng] = p.w + row * wrow_bytes;
-      sp[ng] = p.w_scale + row * srow_bytes;
+      sp[ng] = (WFMT == FP4MOE_W_FP8) ? nullptr : p.w_scale + row * srow_bytes;
     }
-    const uint16_t* ap[MB];
+    // A rows: bf16 [., lda] or MXFP4 codes [., lda/2] + E8M0 [., lda/32]
+    const uint8_t* ap[MB];
+    const uint8_t* asp[MB];
     bool av[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -145,7 +168,14 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
       av[mb] = r < row_end;
       int64_t arow = r;
       if (av[mb] && p.gather) arow = p.gather[r] / p.gather_div;
-      ap[mb] = A + arow * p.lda;
+      if (!av[mb]) arow = 0;
+      if (AFMT == FP4MOE_A_BF16) {
+        ap[mb] = static_cast<const uint8_t*>(p.a) + arow * p.lda * 2;
+        asp[mb] = nullptr;
+      } else {
+        ap[mb] = static_cast<const uint8_t*>(p.a) + arow * (p.lda / 2);
+        asp[mb] = p.a_scale + arow * (p.lda / 32);
+      }
     }
 
     v4f acc[MB][NG];
@@ -156,27 +186,43 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
 
     for (int c = wave; c < nkc; c += 4) {
       const int blk = c * 4 + g;
-      uint4 wv[NG];
+      uint4 wv[NG][2];
       float sc[NG][2];
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) {
-        wv[ng] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 16);
-        if (WFMT == FP4MOE_W_MXFP4) {
-          sc[ng][0] = __uint_as_float((uint32_t)sp[ng][blk] << 23);
-          sc[ng][1] = sc[ng][0];
+        if (WFMT == FP4MOE_W_FP8) {
+          wv[ng][0] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 32);
+          wv[ng][1] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 32 + 16);
+          sc[ng][0] = sc[ng][1] = 1.0f;
         } else {
-          const uint32_t two = *reinterpret_cast<const uint16_t*>(sp[ng] + blk * 2);
-          sc[ng][0] = e4m3_to_f32(two & 0xffu);
-          sc[ng][1] = e4m3_to_f32(two >> 8);
+          wv[ng][0] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 16);
+          wv[ng][1] = wv[ng][0];
+          if (WFMT == FP4MOE_W_MXFP4) {
+            // the convert takes the float's exponent field as an E8M0 byte
+            sc[ng][0] = __uint_as_float((uint32_t)sp[ng][blk] << 23);
+            sc[ng][1] = sc[ng][0];
+          } else {
+            const uint32_t two = *reinterpret_cast<const uint16_t*>(sp[ng] + blk * 2);
+            sc[ng][0] = e4m3_to_f32(two & 0xffu);
+            sc[ng][1] = e4m3_to_f32(two >> 8);
+          }
         }
       }
       uint4 a4[MB][4];
+      float asc[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
+        if (AFMT == FP4MOE_A_BF16) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          a4[mb][s] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 32 + s * 8)
+          for (int s = 0; s < 4; ++s) {
+            a4[mb][s] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 64 + s * 16)
+                               : make_uint4(0, 0, 0, 0);
+          }
+          asc[mb] = 1.0f;
+        } else {
+          a4[mb][0] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 16)
                              : make_uint4(0, 0, 0, 0);
+          asc[mb] = __uint_as_float((uint32_t)(av[mb] ? asp[mb][blk] : 127) << 23);
         }
       }
 #pragma unroll
@@ -184,12 +230,19 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
         v8bf b[NG];
 #pragma unroll
         for (int ng = 0; ng < NG; ++ng) {
-          const uint32_t d = (s == 0) ? wv[ng].x : (s == 1) ? wv[ng].y : (s == 2) ? wv[ng].z : wv[ng].w;
-          b[ng] = (WFMT == FP4MOE_W_MXFP4) ? decode_mx8(d, sc[ng][0]) : decode_nv8(d, sc[ng][s >> 1]);
+          if (WFMT == FP4MOE_W_MXFP4) {
+            b[ng] = decode_mx8(word(wv[ng][0], s), sc[ng][0]);
+          } else if (WFMT == FP4MOE_W_NVFP4) {
+            b[ng] = decode_nv8(word(wv[ng][0], s), sc[ng][s >> 1]);
+          } else {
+            const uint4& h = wv[ng][s >> 1];
+            b[ng] = decode_fp8x8(word(h, (s & 1) * 2), word(h, (s & 1) * 2 + 1));
+          }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const v8bf a = as_bf8(a4[mb][s]);
+          const v8bf a = (AFMT == FP4MOE_A_BF16) ? as_bf8(a4[mb][s])
+                                                 : decode_mx8(word(a4[mb][0], s), asc[mb]);
 #pragma unroll
           for (int ng = 0; ng < NG; ++ng)
             acc[mb][ng] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ng], acc[mb][ng], 0, 0, 0);
@@ -216,7 +269,13 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
           for (int ng = 0; ng < NG; ++ng)
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[mb][ng][i] += red[w][(mb * NG + ng) * 4 + i][lane];
-      const float ts = (WFMT == FP4MOE_W_NVFP4) ? p.w_tensor_scale[e] : 1.0f;
+      float cs[NG];
+#pragma unroll
+      for (int ng = 0; ng < NG; ++ng) {
+        if (WFMT == FP4MOE_W_NVFP4) cs[ng] = p.w_tensor_scale[e];
+        else if (WFMT == FP4MOE_W_FP8) cs[ng] = p.w_channel_scale[(int64_t)e * p.N + wrow[ng]];
+        else cs[ng] = 1.0f;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -224,14 +283,14 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
           const int r = row0 + mb * 16 + g * 4 + i;
           if (r >= row_end) continue;
           if (STAGE == 1) {
-            const float h = silu_mul(acc[mb][0][i] * ts, acc[mb][1][i] * ts);
+            const float h = silu_mul(acc[mb][0][i] * cs[0], acc[mb][1][i] * cs[1]);
             const int64_t o = (int64_t)r * p.ldo + nb * 16 + r16;
             p.out[o] = (uint16_t)f32_to_bf16_rne(h);
             if (p.out_f32) p.out_f32[o] = h;
           } else {
 #pragma unroll
             for (int ng = 0; ng < NG; ++ng) {
-              const float y = acc[mb][ng][i] * ts;
+              const float y = acc[mb][ng][i] * cs[ng];
               const int64_t o = (int64_t)r * p.ldo + nb * 32 + ng * 16 + r16;
               p.out[o] = (uint16_t)f32_to_bf16_rne(y);
               if (p.out_f32) p.out_f32[o] = y;
@@ -251,7 +310,7 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
 // Waves form a 2 x 2 grid over the workgroup tile; each wave owns WM M-blocks
 // and WN weight-row blocks of 16.  Stage 1 pairs gate block j with up block
 // j + WN/2 so SiLU(gate)*up is lane-local.
-template <int WFMT, int STAGE, int WM, int WN>
+template <int STAGE, int WM, int WN>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r16 = lane & 15;
@@ -262,7 +321,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int n_nb = n_out / OUT_PER_WG;
   const int nkc = p.K / 128;
-  const int64_t wrow_bytes = (WFMT == FP4MOE_W_FP8) ? p.K : p.K / 2;
+  const int64_t wrow_bytes = p.K / 2;
   const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
   const uint8_t* A = static_cast<const uint8_t*>(p.a);
   const int64_t a_row_bytes = p.lda / 2, a_srow = p.lda / 32;
@@ -289,7 +348,6 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
     }
     const uint8_t* wp[WN];
     const uint8_t* sp[WN];
-    int wrow[WN];
 #pragma unroll
     for (int nbk = 0; nbk < WN; ++nbk) {
       int wr;
@@ -298,10 +356,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
       } else {
         wr = col0 + nbk * 16 + r16;
       }
-      wrow[nbk] = wr;
       const int64_t row = (int64_t)e * p.N + wr;
       wp[nbk] = p.w + row * wrow_bytes;
-      sp[nbk] = (WFMT == FP4MOE_W_MXFP4) ? p.w_scale + row * (p.K / 32) : nullptr;
+      sp[nbk] = p.w_scale + row * (p.K / 32);
     }
 
     v4f acc[WM][WN];
@@ -329,36 +386,19 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
       int bs[WN];
 #pragma unroll
       for (int nbk = 0; nbk < WN; ++nbk) {
-        if (WFMT == FP4MOE_W_MXFP4) {
-          const uint4 v = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 16);
-          bf[nbk] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-          bs[nbk] = sp[nbk][blk];
-        } else {
-          const uint4 v0 = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 32);
-          const uint4 v1 = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 32 + 16);
-          bf[nbk] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-          bs[nbk] = 127;
-        }
+        const uint4 v = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 16);
+        bf[nbk] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+        bs[nbk] = sp[nbk][blk];
       }
 #pragma unroll
       for (int mb = 0; mb < WM; ++mb)
 #pragma unroll
-        for (int nbk = 0; nbk < WN; ++nbk) {
-          if (WFMT == FP4MOE_W_MXFP4)
-            acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[mb], bf[nbk], acc[mb][nbk], 4, 4, 0, as[mb], 0, bs[nbk]);
-          else
-            acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[mb], bf[nbk], acc[mb][nbk], 4, 0, 0, as[mb], 0, bs[nbk]);
-        }
+        for (int nbk = 0; nbk < WN; ++nbk)
+          acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[mb], bf[nbk], acc[mb][nbk], 4, 4, 0, as[mb], 0, bs[nbk]);
     }
 
     // epilogue
-    float cs[WN];
-#pragma unroll
-    for (int nbk = 0; nbk < WN; ++nbk)
-      cs[nbk] = (WFMT == FP4MOE_W_FP8) ? p.w_channel_scale[(int64_t)e * p.N + wrow[nbk]] : 1.0f;
 #pragma unroll
     for (int mb = 0; mb < WM; ++mb) {
 #pragma unroll
@@ -368,7 +408,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
         if (STAGE == 1) {
 #pragma unroll
           for (int j = 0; j < WN / 2; ++j) {
-            const float h = silu_mul(acc[mb][j][i] * cs[j], acc[mb][j + WN / 2][i] * cs[j + WN / 2]);
+            const float h = silu_mul(acc[mb][j][i], acc[mb][j + WN / 2][i]);
             const int64_t o = (int64_t)r * p.ldo + col0 + j * 16 + r16;
             p.out[o] = (uint16_t)f32_to_bf16_rne(h);
             if (p.out_f32) p.out_f32[o] = h;
@@ -376,7 +416,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
         } else {
 #pragma unroll
           for (int nbk = 0; nbk < WN; ++nbk) {
-            const float y = acc[mb][nbk][i] * cs[nbk];
+            const float y = acc[mb][nbk][i];
             const int64_t o = (int64_t)r * p.ldo + col0 + nbk * 16 + r16;
             p.out[o] = (uint16_t)f32_to_bf16_rne(y);
             if (p.out_f32) p.out_f32[o] = y;
@@ -404,35 +444,41 @@ static int grid_cap() {
   return g_num_cus * 8;
 }
 
-template <int WFMT, int STAGE>
+template <int WFMT, int AFMT, int STAGE>
 static void launch_dq(const GemmParams& p, int max_tiles, hipStream_t s) {
   const int n_nb = (STAGE == 1) ? (p.N / 2) / 16 : p.N / 32;
   int64_t work = (int64_t)max_tiles * n_nb;
   const int grid = (int)(work < grid_cap() ? (work < 1 ? 1 : work) : grid_cap());
   switch (p.block_m) {
-    case 16: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 1>), dim3(grid), dim3(256), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 2>), dim3(grid), dim3(256), 0, s, p); break;
-    default: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, STAGE, 4>), dim3(grid), dim3(256), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, AFMT, STAGE, 1>), dim3(grid), dim3(256), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, AFMT, STAGE, 2>), dim3(grid), dim3(256), 0, s, p); break;
+    default: hipLaunchKernelGGL((dq_gemm_kernel<WFMT, AFMT, STAGE, 4>), dim3(grid), dim3(256), 0, s, p); break;
   }
 }
 
-template <int WFMT, int STAGE, int WM>
+template <int WFMT, int AFMT>
+static void launch_dq_stage(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
+  if (stage == 1) launch_dq<WFMT, AFMT, 1>(p, max_tiles, s);
+  else launch_dq<WFMT, AFMT, 2>(p, max_tiles, s);
+}
+
+template <int STAGE, int WM>
 static void launch_mx_wm(const GemmParams& p, int max_tiles, hipStream_t s) {
   constexpr int WN = 4;
   const int out_per_wg = 2 * ((STAGE == 1) ? (WN / 2) * 16 : WN * 16);
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
   const int grid = (int)(work < grid_cap() ? (work < 1 ? 1 : work) : grid_cap());
-  hipLaunchKernelGGL((mx_gemm_kernel<WFMT, STAGE, WM, WN>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((mx_gemm_kernel<STAGE, WM, WN>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int WFMT, int STAGE>
+template <int STAGE>
 static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
   switch (p.block_m) {
-    case 32: launch_mx_wm<WFMT, STAGE, 1>(p, max_tiles, s); break;
-    case 64: launch_mx_wm<WFMT, STAGE, 2>(p, max_tiles, s); break;
-    case 128: launch_mx_wm<WFMT, STAGE, 4>(p, max_tiles, s); break;
-    default: launch_mx_wm<WFMT, STAGE, 8>(p, max_tiles, s); break;
+    case 32: launch_mx_wm<STAGE, 1>(p, max_tiles, s); break;
+    case 64: launch_mx_wm<STAGE, 2>(p, max_tiles, s); break;
+    case 128: launch_mx_wm<STAGE, 4>(p, max_tiles, s); break;
+    default: launch_mx_wm<STAGE, 8>(p, max_tiles, s); break;
   }
 }
 
@@ -443,21 +489,24 @@ using namespace fp4moe;
 extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a, "fp4_grouped_gemm: null args");
   FP4MOE_REQUIRE(a->stage == 1 || a->stage == 2, "fp4_grouped_gemm: stage=%d", a->stage);
-  const bool dq = a->afmt == FP4MOE_A_BF16;
-  const bool mx = a->afmt == FP4MOE_A_MXFP4;
-  FP4MOE_REQUIRE((dq && (a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4)) ||
-                     (mx && (a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_FP8)),
-                 "fp4_grouped_gemm: unsupported (wfmt=%d, afmt=%d)", a->wfmt, a->afmt);
+  const bool mx = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_MXFP4;
+  const bool dq = !mx;
+  FP4MOE_REQUIRE(a->afmt == FP4MOE_A_BF16 || a->afmt == FP4MOE_A_MXFP4,
+                 "fp4_grouped_gemm: afmt=%d", a->afmt);
+  FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4 || a->wfmt == FP4MOE_W_FP8,
+                 "fp4_grouped_gemm: wfmt=%d", a->wfmt);
+  FP4MOE_REQUIRE(!(a->wfmt == FP4MOE_W_NVFP4 && a->afmt == FP4MOE_A_MXFP4),
+                 "fp4_grouped_gemm: NVFP4 weights take bf16 activations (nvfp4_qdq output)");
   FP4MOE_REQUIRE(a->K > 0 && a->K % 128 == 0, "fp4_grouped_gemm: K=%d not a multiple of 128", a->K);
   FP4MOE_REQUIRE(a->N > 0 && a->N % 32 == 0 && (a->stage == 2 || a->N % 64 == 0),
                  "fp4_grouped_gemm: N=%d (stage %d)", a->N, a->stage);
   if (dq) {
     FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64,
-                   "fp4_grouped_gemm: block_m=%d not in {16,32,64} for bf16 activations",
+                   "fp4_grouped_gemm: block_m=%d not in {16,32,64} for this format pair",
                    a->block_m);
   } else {
     FP4MOE_REQUIRE(a->block_m == 32 || a->block_m == 64 || a->block_m == 128 || a->block_m == 256,
-                   "fp4_grouped_gemm: block_m=%d not in {32,64,128,256} for MXFP4 activations",
+                   "fp4_grouped_gemm: block_m=%d not in {32,64,128,256} for MXFP4 x MXFP4",
                    a->block_m);
     const int out_per_wg = a->stage == 1 ? 64 : 128;
     const int n_out = a->stage == 1 ? a->N / 2 : a->N;
@@ -480,7 +529,8 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: NVFP4 needs w_tensor_scale");
   FP4MOE_REQUIRE(a->wfmt != FP4MOE_W_FP8 || a->w_channel_scale,
                  "fp4_grouped_gemm: FP8 needs w_channel_scale");
-  FP4MOE_REQUIRE(!mx || a->a_scale, "fp4_grouped_gemm: MXFP4 activations need a_scale");
+  FP4MOE_REQUIRE(a->afmt != FP4MOE_A_MXFP4 || a->a_scale,
+                 "fp4_grouped_gemm: MXFP4 activations need a_scale");
   FP4MOE_REQUIRE(((uintptr_t)a->w & 15) == 0 && ((uintptr_t)a->a & 15) == 0,
                  "fp4_grouped_gemm: w and a must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
@@ -507,22 +557,16 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.out_f32 = a->out_f32;
   hipStream_t s = as_stream(stream);
   const int mt = a->max_tiles;
-  if (dq) {
-    if (a->wfmt == FP4MOE_W_MXFP4) {
-      if (a->stage == 1) launch_dq<FP4MOE_W_MXFP4, 1>(p, mt, s);
-      else launch_dq<FP4MOE_W_MXFP4, 2>(p, mt, s);
-    } else {
-      if (a->stage == 1) launch_dq<FP4MOE_W_NVFP4, 1>(p, mt, s);
-      else launch_dq<FP4MOE_W_NVFP4, 2>(p, mt, s);
-    }
+  const int st = a->stage;
+  if (mx) {
+    if (st == 1) launch_mx<1>(p, mt, s);
+    else launch_mx<2>(p, mt, s);
+  } else if (a->afmt == FP4MOE_A_BF16) {
+    if (a->wfmt == FP4MOE_W_MXFP4) launch_dq_stage<FP4MOE_W_MXFP4, FP4MOE_A_BF16>(p, st, mt, s);
+    else if (a->wfmt == FP4MOE_W_NVFP4) launch_dq_stage<FP4MOE_W_NVFP4, FP4MOE_A_BF16>(p, st, mt, s);
+    else launch_dq_stage<FP4MOE_W_FP8, FP4MOE_A_BF16>(p, st, mt, s);
   } else {
-    if (a->wfmt == FP4MOE_W_MXFP4) {
-      if (a->stage == 1) launch_mx<FP4MOE_W_MXFP4, 1>(p, mt, s);
-      else launch_mx<FP4MOE_W_MXFP4, 2>(p, mt, s);
-    } else {
-      if (a->stage == 1) launch_mx<FP4MOE_W_FP8, 1>(p, mt, s);
-      else launch_mx<FP4MOE_W_FP8, 2>(p, mt, s);
-    }
+    launch_dq_stage<FP4MOE_W_FP8, FP4MOE_A_MXFP4>(p, st, mt, s);
   }
   return check_launch("fp4_grouped_gemm");
 }

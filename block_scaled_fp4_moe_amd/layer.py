@@ -81,21 +81,27 @@ class MoELayer:
         self._bufs[T] = b
         return b
 
-    def forward(self, x, logits, bias, keep=False, stream=None):
+    def forward(self, x, logits, bias, keep=False, stream=None, events=None):
         """x bf16 [T, H], logits float32 [T, E], bias float32 [E] -> out bf16 [T, H].
 
-        With keep=True returns the dict of every intermediate buffer."""
+        With keep=True returns the dict of every intermediate buffer.  `events`
+        (optional) maps a step name ("stage1", "stage2", ...) to a list that
+        receives a (start, end) pair of recorded HIP events for that call."""
         c = self.cfg
+        tick = _Ticker(events, stream)
         T = x.shape[0]
         k = c.topk + c.n_shared
         b = self._buffers(T)
+        tick("route")
         moe_route(logits, bias, c.n_group, c.topk_group, c.topk, c.renormalize, c.routed_scale,
                   topk_ids=b["topk_ids"], topk_w=b["topk_w"], stream=stream)
+        tick("permute")
         perm = moe_permute(b["topk_ids"], c.E, c.n_shared, c.block_m, workspace=b["perm_ws"],
                            out=b["perm"], stream=stream)
         n_rows = perm["expert_offsets"][c.E + c.n_shared:]     # device row count
         wf = WFMT[c.wfmt]
         w = self.w
+        tick("quant1")
         if c.afmt == "mx":
             mxfp4_quant_1x32(x, codes=b["xq"], scales=b["xs"], stream=stream)
             a1, a1s, af = b["xq"], b["xs"], A_MXFP4
@@ -106,10 +112,12 @@ class MoELayer:
             a1, a1s, af = x, None, A_BF16
         ts13 = w.get("w13_ts") if c.wfmt == "nvfp4" else None
         cs13 = w["w13_scale"] if c.wfmt == "fp8" else None
+        tick("stage1")
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
                          a_row_gather=perm["sorted_pairs"], gather_div=k, out=b["h"],
                          stream=stream)
+        tick("quant2")
         if c.afmt == "mx":
             mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
                              stream=stream)
@@ -122,9 +130,31 @@ class MoELayer:
             a2, a2s = b["h"], None
         ts2 = w.get("w2_ts") if c.wfmt == "nvfp4" else None
         cs2 = w["w2_scale"] if c.wfmt == "fp8" else None
+        tick("stage2")
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
                          c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
                          out=b["y"], stream=stream)
+        tick("combine")
         moe_combine(b["y"], perm["pair_pos"], b["topk_w"], c.topk, c.n_shared, out=b["out"],
                     stream=stream)
+        tick(None)
         return b if keep else b["out"]
+
+
+class _Ticker:
+    """Records a HIP event between consecutive steps when `events` is given."""
+
+    def __init__(self, events, stream):
+        self.events = events
+        self.stream = stream
+        self.name = None
+        self.start = None
+
+    def __call__(self, name):
+        if self.events is None:
+            return
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(self.stream if self.stream is not None else torch.cuda.current_stream())
+        if self.name is not None:
+            self.events.setdefault(self.name, []).append((self.start, ev))
+        self.name, self.start = name, ev

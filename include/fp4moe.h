@@ -159,9 +159,12 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * expert_offsets[e+1]-1; the tile list comes from moe_permute with the same
  * block_m.  A row r is read from A row a_row_gather[r] / gather_div when
  * a_row_gather != NULL (stage 1 passes sorted_pairs and k), else row r.
- * Supported (wfmt, afmt): (MXFP4, BF16), (NVFP4, BF16), (MXFP4, MXFP4),
- * (FP8, MXFP4).  K % 128 == 0, N % 32 == 0 (stage 1: N % 64 == 0);
- * block_m in {16, 32, 64} for afmt BF16 and {32, 64, 128, 256} for MXFP4.
+ * Supported (wfmt, afmt): (MXFP4, BF16), (NVFP4, BF16), (FP8, BF16),
+ * (FP8, MXFP4) -- operands decoded exactly to bf16 in registers, bf16 MFMA --
+ * and (MXFP4, MXFP4) -- gfx950 scaled MFMA FP4 x FP4.  K % 128 == 0,
+ * N % 32 == 0 (stage 1: N % 64 == 0); block_m in {32, 64, 128, 256} for
+ * (MXFP4, MXFP4) with the output width a multiple of 64 (stage 1) or 128
+ * (stage 2), block_m in {16, 32, 64} otherwise.
  */
 typedef struct {
   int stage;               /* 1 or 2                                                */

@@ -85,10 +85,12 @@ def test_gemm_rejects_unsupported_combinations():
                            None, a["ldo"], None)
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
-    assert run(wfmt=2, afmt=0)[0] == 1          # FP8 weights need MXFP4 activations
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
+    assert run(wfmt=3)[0] == 1
+    assert run(afmt=2)[0] == 1
     assert run(K=96)[0] == 1
     assert run(block_m=128)[0] == 1             # bf16 path tiles are 16/32/64 rows
+    assert run(wfmt=2, afmt=1, block_m=128)[0] == 1
     assert run(afmt=1, block_m=16)[0] == 1
     assert run(N=96)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers

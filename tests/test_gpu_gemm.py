@@ -137,6 +137,8 @@ DQ_CASES = [
     (1, "nvfp4", 60, 4, 8, 0, 512, 256, 64, 9, True),
     (2, "nvfp4", 60, 4, 8, 0, 512, 256, 64, 10, True),
     (1, "nvfp4", 40, 2, 12, 0, 1024, 512, 16, 11, False),
+    (1, "fp8", 50, 2, 6, 1, 512, 256, 16, 12, True),
+    (2, "fp8", 50, 2, 6, 1, 512, 256, 64, 13, True),
 ]
 
 
@@ -156,7 +158,8 @@ MX_CASES = [
     (1, "mx", 5, 2, 4, 1, 7168, 2048, 32, 27, False),
     (2, "mx", 5, 2, 4, 1, 7168, 2048, 32, 28, False),
     (1, "fp8", 150, 3, 6, 1, 512, 256, 64, 29, True),
-    (2, "fp8", 150, 3, 6, 1, 512, 256, 128, 30, True),
+    (2, "fp8", 150, 3, 6, 1, 512, 256, 32, 30, True),
+    (1, "fp8", 3, 2, 4, 1, 7168, 2048, 16, 32, False),
 ]
 
 
