@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libfp4moe.so")
 
 W_MXFP4, W_NVFP4, W_FP8 = 0, 1, 2
 A_BF16, A_MXFP4 = 0, 1
+LAYOUT_ROWMAJOR, LAYOUT_FRAGMENT = 0, 1
 WFMT = {"mx": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8}
 
 _lib = None
@@ -43,6 +44,7 @@ class GemmArgs(ctypes.Structure):
         ("a_row_gather", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
         ("tiles", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_f32", ctypes.c_void_p),
+        ("w_layout", ctypes.c_int),
     ]
 
 
@@ -67,6 +69,7 @@ def load():
         "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, S, P], I),
         "fp4_grouped_gemm": ([ctypes.POINTER(GemmArgs), P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P, P], I),
+        "fp4_weight_preshuffle": ([I, I, I, I, P, P, P, P, P], I),
         "mxfp4_to_fp8_channel": ([P, P, I64, I, P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
@@ -188,7 +191,8 @@ def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=N
 
 def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale=None,
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
-                     gather_div=1, out=None, out_f32=None, max_rows=None, stream=None):
+                     gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
+                     stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
@@ -215,9 +219,25 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     None if a_row_gather is None else a_row_gather.data_ptr(),
                     perm["expert_offsets"].data_ptr(), perm["tiles"].data_ptr(),
                     perm["n_tiles"].data_ptr(), out.data_ptr(), out.stride(0),
-                    None if out_f32 is None else out_f32.data_ptr())
+                    None if out_f32 is None else out_f32.data_ptr(), w_layout)
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
+
+
+def fp4_weight_preshuffle(wfmt, codes, scales=None, codes_out=None, scales_out=None,
+                          stream=None):
+    """Expert weights [E, N, K/2] (FP8 [E, N, K]) + scales -> fragment-major copies."""
+    lib = load()
+    E, N = codes.shape[0], codes.shape[1]
+    K = codes.shape[2] if wfmt == W_FP8 else codes.shape[2] * 2
+    if codes_out is None:
+        codes_out = torch.empty_like(codes)
+    if scales is not None and scales_out is None and wfmt != W_FP8:
+        scales_out = torch.empty_like(scales)
+    _check(lib.fp4_weight_preshuffle(wfmt, E, N, K, _p(codes), _p(scales if wfmt != W_FP8 else None),
+                                     _p(codes_out), _p(scales_out if wfmt != W_FP8 else None),
+                                     _stream(stream)))
+    return codes_out, (scales_out if wfmt != W_FP8 else scales)
 
 
 def moe_combine(y, pair_pos, topk_w, topk, n_shared, out=None, out_f32=None, stream=None):

@@ -45,7 +45,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 struct GemmParams {
-  int N, K, n_experts, block_m, gather_div;
+  int N, K, n_experts, block_m, gather_div, w_layout;
   int64_t lda, ldo;
   const uint8_t* w;
   const uint8_t* w_scale;
@@ -129,6 +129,7 @@ __device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf
 template <int WFMT, int AFMT, int STAGE, int MB>
 __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
   constexpr int NG = 2;            // two 16-row weight groups per work item
+  constexpr int U = (MB == 1) ? 4 : (MB == 2 ? 2 : 1);   // chunks in flight per wave
   constexpr int NV = MB * NG * 4;  // accumulator floats per lane
   __shared__ float red[3][NV][64];
 
@@ -147,16 +148,33 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
     const int row0 = p.offsets[e] + mt * BM;
     const int row_end = min(p.offsets[e + 1], row0 + BM);
 
+    // Per lane and weight group: code / scale address of chunk 0 and the
+    // stride between chunks, for the row-major or the fragment-major layout.
     const uint8_t* wp[NG];
     const uint8_t* sp[NG];
     int wrow[NG];
+    int64_t wstride, sstride, whalf;
 #pragma unroll
     for (int ng = 0; ng < NG; ++ng) {
       const int wr = (STAGE == 1) ? (ng * (p.N / 2) + nb * 16 + r16) : (nb * 32 + ng * 16 + r16);
       wrow[ng] = wr;
-      const int64_t row = (int64_t)e * p.N + wr;
-      wp[ng] = p.w + row * wrow_bytes;
-      sp[ng] = (WFMT == FP4MOE_W_FP8) ? nullptr : p.w_scale + row * srow_bytes;
+      if (p.w_layout == 0) {
+        const int64_t row = (int64_t)e * p.N + wr;
+        wp[ng] = p.w + row * wrow_bytes + g * (WFMT == FP4MOE_W_FP8 ? 32 : 16);
+        sp[ng] = (WFMT == FP4MOE_W_FP8) ? nullptr
+                                        : p.w_scale + row * srow_bytes + g * (WFMT == FP4MOE_W_MXFP4 ? 1 : 2);
+        wstride = (WFMT == FP4MOE_W_FP8) ? 128 : 64;
+        whalf = 16;
+        sstride = (WFMT == FP4MOE_W_MXFP4) ? 4 : 8;
+      } else {
+        const int64_t f0 = ((int64_t)e * (p.N / 16) + wr / 16) * nkc;
+        wstride = (WFMT == FP4MOE_W_FP8) ? 2048 : 1024;
+        whalf = 1024;
+        wp[ng] = p.w + f0 * wstride + lane * 16;
+        sstride = (WFMT == FP4MOE_W_MXFP4) ? 64 : 128;
+        sp[ng] = (WFMT == FP4MOE_W_FP8) ? nullptr
+                                        : p.w_scale + f0 * sstride + lane * (WFMT == FP4MOE_W_MXFP4 ? 1 : 2);
+      }
     }
     // A rows: bf16 [., lda] or MXFP4 codes [., lda/2] + E8M0 [., lda/32]
     const uint8_t* ap[MB];
@@ -184,68 +202,82 @@ __global__ __launch_bounds__(256) void dq_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) acc[mb][ng] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int c = wave; c < nkc; c += 4) {
-      const int blk = c * 4 + g;
-      uint4 wv[NG][2];
-      float sc[NG][2];
+    // K chunks go round-robin over the four waves; each step of a wave takes
+    // U of its chunks and issues all their loads before the first MFMA, so a
+    // wave keeps U*NG 16-byte weight loads per lane in flight.
+    for (int c0 = wave; c0 < nkc; c0 += 4 * U) {
+      uint4 wv[U][NG][2];
+      float sc[U][NG][2];
+      uint4 a4[U][MB][4];
+      float asc[U][MB];
 #pragma unroll
-      for (int ng = 0; ng < NG; ++ng) {
-        if (WFMT == FP4MOE_W_FP8) {
-          wv[ng][0] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 32);
-          wv[ng][1] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 32 + 16);
-          sc[ng][0] = sc[ng][1] = 1.0f;
-        } else {
-          wv[ng][0] = *reinterpret_cast<const uint4*>(wp[ng] + blk * 16);
-          wv[ng][1] = wv[ng][0];
-          if (WFMT == FP4MOE_W_MXFP4) {
-            // the convert takes the float's exponent field as an E8M0 byte
-            sc[ng][0] = __uint_as_float((uint32_t)sp[ng][blk] << 23);
-            sc[ng][1] = sc[ng][0];
-          } else {
-            const uint32_t two = *reinterpret_cast<const uint16_t*>(sp[ng] + blk * 2);
-            sc[ng][0] = e4m3_to_f32(two & 0xffu);
-            sc[ng][1] = e4m3_to_f32(two >> 8);
-          }
-        }
-      }
-      uint4 a4[MB][4];
-      float asc[MB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        if (AFMT == FP4MOE_A_BF16) {
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            a4[mb][s] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 64 + s * 16)
-                               : make_uint4(0, 0, 0, 0);
-          }
-          asc[mb] = 1.0f;
-        } else {
-          a4[mb][0] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 16)
-                             : make_uint4(0, 0, 0, 0);
-          asc[mb] = __uint_as_float((uint32_t)(av[mb] ? asp[mb][blk] : 127) << 23);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        v8bf b[NG];
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 4 * u;
+        if (c >= nkc) break;
+        const int blk = c * 4 + g;
 #pragma unroll
         for (int ng = 0; ng < NG; ++ng) {
-          if (WFMT == FP4MOE_W_MXFP4) {
-            b[ng] = decode_mx8(word(wv[ng][0], s), sc[ng][0]);
-          } else if (WFMT == FP4MOE_W_NVFP4) {
-            b[ng] = decode_nv8(word(wv[ng][0], s), sc[ng][s >> 1]);
+          const uint8_t* wc = wp[ng] + (int64_t)c * wstride;
+          if (WFMT == FP4MOE_W_FP8) {
+            wv[u][ng][0] = *reinterpret_cast<const uint4*>(wc);
+            wv[u][ng][1] = *reinterpret_cast<const uint4*>(wc + whalf);
+            sc[u][ng][0] = sc[u][ng][1] = 1.0f;
           } else {
-            const uint4& h = wv[ng][s >> 1];
-            b[ng] = decode_fp8x8(word(h, (s & 1) * 2), word(h, (s & 1) * 2 + 1));
+            wv[u][ng][0] = *reinterpret_cast<const uint4*>(wc);
+            wv[u][ng][1] = wv[u][ng][0];
+            const uint8_t* scp = sp[ng] + (int64_t)c * sstride;
+            if (WFMT == FP4MOE_W_MXFP4) {
+              // the convert takes the float's exponent field as an E8M0 byte
+              sc[u][ng][0] = __uint_as_float((uint32_t)*scp << 23);
+              sc[u][ng][1] = sc[u][ng][0];
+            } else {
+              const uint32_t two = *reinterpret_cast<const uint16_t*>(scp);
+              sc[u][ng][0] = e4m3_to_f32(two & 0xffu);
+              sc[u][ng][1] = e4m3_to_f32(two >> 8);
+            }
           }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const v8bf a = (AFMT == FP4MOE_A_BF16) ? as_bf8(a4[mb][s])
-                                                 : decode_mx8(word(a4[mb][0], s), asc[mb]);
+          if (AFMT == FP4MOE_A_BF16) {
 #pragma unroll
-          for (int ng = 0; ng < NG; ++ng)
-            acc[mb][ng] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ng], acc[mb][ng], 0, 0, 0);
+            for (int s = 0; s < 4; ++s) {
+              a4[u][mb][s] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 64 + s * 16)
+                                    : make_uint4(0, 0, 0, 0);
+            }
+            asc[u][mb] = 1.0f;
+          } else {
+            a4[u][mb][0] = av[mb] ? *reinterpret_cast<const uint4*>(ap[mb] + blk * 16)
+                                  : make_uint4(0, 0, 0, 0);
+            asc[u][mb] = __uint_as_float((uint32_t)(av[mb] ? asp[mb][blk] : 127) << 23);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (c0 + 4 * u >= nkc) break;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          v8bf b[NG];
+#pragma unroll
+          for (int ng = 0; ng < NG; ++ng) {
+            if (WFMT == FP4MOE_W_MXFP4) {
+              b[ng] = decode_mx8(word(wv[u][ng][0], s), sc[u][ng][0]);
+            } else if (WFMT == FP4MOE_W_NVFP4) {
+              b[ng] = decode_nv8(word(wv[u][ng][0], s), sc[u][ng][s >> 1]);
+            } else {
+              const uint4& h = wv[u][ng][s >> 1];
+              b[ng] = decode_fp8x8(word(h, (s & 1) * 2), word(h, (s & 1) * 2 + 1));
+            }
+          }
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const v8bf a = (AFMT == FP4MOE_A_BF16) ? as_bf8(a4[u][mb][s])
+                                                   : decode_mx8(word(a4[u][mb][0], s), asc[u][mb]);
+#pragma unroll
+            for (int ng = 0; ng < NG; ++ng)
+              acc[mb][ng] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ng], acc[mb][ng], 0, 0, 0);
+          }
         }
       }
     }
@@ -356,10 +388,18 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
       } else {
         wr = col0 + nbk * 16 + r16;
       }
-      const int64_t row = (int64_t)e * p.N + wr;
-      wp[nbk] = p.w + row * wrow_bytes;
-      sp[nbk] = p.w_scale + row * (p.K / 32);
+      if (p.w_layout == 0) {
+        const int64_t row = (int64_t)e * p.N + wr;
+        wp[nbk] = p.w + row * wrow_bytes + g * 16;
+        sp[nbk] = p.w_scale + row * (p.K / 32) + g;
+      } else {
+        const int64_t f0 = ((int64_t)e * (p.N / 16) + wr / 16) * nkc;
+        wp[nbk] = p.w + f0 * 1024 + lane * 16;
+        sp[nbk] = p.w_scale + f0 * 64 + lane;
+      }
     }
+    const int64_t wstride = (p.w_layout == 0) ? 64 : 1024;
+    const int64_t sstride = (p.w_layout == 0) ? 4 : 64;
 
     v4f acc[WM][WN];
 #pragma unroll
@@ -386,9 +426,9 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(GemmParams p) {
       int bs[WN];
 #pragma unroll
       for (int nbk = 0; nbk < WN; ++nbk) {
-        const uint4 v = *reinterpret_cast<const uint4*>(wp[nbk] + blk * 16);
+        const uint4 v = *reinterpret_cast<const uint4*>(wp[nbk] + (int64_t)c * wstride);
         bf[nbk] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        bs[nbk] = sp[nbk][blk];
+        bs[nbk] = sp[nbk][(int64_t)c * sstride];
       }
 #pragma unroll
       for (int mb = 0; mb < WM; ++mb)
@@ -517,6 +557,10 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: n_experts=%d max_rows=%d max_tiles=%d", a->n_experts,
                  a->max_rows, a->max_tiles);
   FP4MOE_REQUIRE(a->gather_div >= 1, "fp4_grouped_gemm: gather_div=%d", a->gather_div);
+  FP4MOE_REQUIRE(a->w_layout == FP4MOE_LAYOUT_ROWMAJOR || a->w_layout == FP4MOE_LAYOUT_FRAGMENT,
+                 "fp4_grouped_gemm: w_layout=%d", a->w_layout);
+  FP4MOE_REQUIRE(a->w_layout == FP4MOE_LAYOUT_ROWMAJOR || a->N % 16 == 0,
+                 "fp4_grouped_gemm: fragment layout needs N %% 16 == 0");
   const int n_out = a->stage == 1 ? a->N / 2 : a->N;
   FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
   FP4MOE_REQUIRE(a->lda >= a->K && a->lda % 32 == 0, "fp4_grouped_gemm: lda=%lld",
@@ -541,6 +585,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.n_experts = a->n_experts;
   p.block_m = a->block_m;
   p.gather_div = a->gather_div;
+  p.w_layout = a->w_layout;
   p.lda = a->lda;
   p.ldo = a->ldo;
   p.w = a->w;

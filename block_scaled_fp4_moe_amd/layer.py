@@ -12,8 +12,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (A_BF16, A_MXFP4, WFMT, fp4_grouped_gemm, moe_combine, moe_permute,
-               moe_permute_max_tiles, moe_route, mxfp4_quant_1x32, nvfp4_qdq, load)
+from . import (A_BF16, A_MXFP4, LAYOUT_FRAGMENT, LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm,
+               fp4_weight_preshuffle, moe_combine, moe_permute, moe_permute_max_tiles, moe_route,
+               mxfp4_quant_1x32, nvfp4_qdq, load)
 
 
 @dataclass
@@ -30,17 +31,32 @@ class LayerConfig:
     block_m: int = 16
     renormalize: bool = True
     routed_scale: float = 1.0
+    fragment_layout: bool = True   # stream weights from the fragment-major layout
 
 
 class MoELayer:
     """Weights (device tensors):
          w13 [E+n_shared, 2I, H/2] (FP8: [.., H]), w13_scale (E8M0 [.., H/32] |
          E4M3 [.., H/16] | float32 channel scale [E+n_shared, 2I]), w13_ts float32
-         [E+n_shared] for NVFP4; w2 / w2_scale / w2_ts likewise with [H, I]."""
+         [E+n_shared] for NVFP4; w2 / w2_scale / w2_ts likewise with [H, I],
+         all in the row-major layout.  With cfg.fragment_layout the codes and
+         block scales are rewritten once, here, by fp4_weight_preshuffle (the
+         row-major tensors are then no longer referenced).  Pass
+         preshuffled=True when the weights already are fragment-major."""
 
-    def __init__(self, cfg: LayerConfig, weights: dict, device="cuda"):
+    def __init__(self, cfg: LayerConfig, weights: dict, device="cuda", preshuffled=False):
         load()
         self.cfg = cfg
+        self.layout = LAYOUT_FRAGMENT if cfg.fragment_layout else LAYOUT_ROWMAJOR
+        if cfg.fragment_layout and not preshuffled:
+            weights = dict(weights)
+            wf = WFMT[cfg.wfmt]
+            for name in ("w13", "w2"):
+                sc = None if cfg.wfmt == "fp8" else weights[name + "_scale"]
+                c, s = fp4_weight_preshuffle(wf, weights[name], sc)
+                weights[name] = c
+                if cfg.wfmt != "fp8":
+                    weights[name + "_scale"] = s
         self.w = weights
         self.device = device
         self._bufs = {}
@@ -116,7 +132,7 @@ class MoELayer:
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
                          a_row_gather=perm["sorted_pairs"], gather_div=k, out=b["h"],
-                         stream=stream)
+                         w_layout=self.layout, stream=stream)
         tick("quant2")
         if c.afmt == "mx":
             mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
@@ -133,7 +149,7 @@ class MoELayer:
         tick("stage2")
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
                          c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
-                         out=b["y"], stream=stream)
+                         out=b["y"], w_layout=self.layout, stream=stream)
         tick("combine")
         moe_combine(b["y"], perm["pair_pos"], b["topk_w"], c.topk, c.n_shared, out=b["out"],
                     stream=stream)

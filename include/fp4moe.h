@@ -51,6 +51,12 @@ enum {
   FP4MOE_W_FP8 = 2     /* E4M3 codes [E,N,K] + fp32 per-row channel scale [E,N]              */
 };
 
+/* Weight layouts of fp4_grouped_gemm (see fp4_weight_preshuffle). */
+enum {
+  FP4MOE_LAYOUT_ROWMAJOR = 0,  /* codes [E,N,K/2] (FP8 [E,N,K]), scales [E,N,K/32|K/16]       */
+  FP4MOE_LAYOUT_FRAGMENT = 1   /* fragment-major, produced by fp4_weight_preshuffle          */
+};
+
 /* Activation formats of fp4_grouped_gemm. */
 enum {
   FP4MOE_A_BF16 = 0,   /* bf16 [rows, K]: weights are decoded to bf16 inside the GEMM tile  */
@@ -191,9 +197,31 @@ typedef struct {
   uint16_t* out;           /* bf16 [max_rows, ldo]                                 */
   int64_t ldo;             /* out row stride in elements                           */
   float* out_f32;          /* optional float32 copy before bf16 rounding, stride ldo */
+  int w_layout;            /* FP4MOE_LAYOUT_* of w and w_scale                      */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);
+
+/*
+ * fp4_weight_preshuffle -- rewrite static expert weights into the
+ * fragment-major layout (FP4MOE_LAYOUT_FRAGMENT) that fp4_grouped_gemm
+ * streams with one contiguous KiB per wavefront load.
+ * [ATOM] "Stage C: MXFP4 Linear GEMM": the production FP4 GEMMs take their
+ * weight operand pre-shuffled for the matrix instruction; this layout is our
+ * own, derived from the MFMA operand layout of our kernels.
+ * With G = N/16 row groups, C = K/128 chunks, f = (e*G + n/16)*C + k/128 and
+ * lane = n%16 + 16*((k%128)/32), element (e, n, k) goes to
+ *   FP4 codes   byte f*1024 + lane*16 + (k%32)/2   (same nibble as before)
+ *   FP8 codes   byte f*2048 + ((k%32)/16)*1024 + lane*16 + k%16
+ *   E8M0 scale  byte f*64 + lane                     (MXFP4, per 32 along k)
+ *   E4M3 scale  byte f*128 + lane*2 + (k%32)/16      (NVFP4, per 16 along k)
+ * FP8 channel scales and NVFP4 tensor scales keep their layout.  Same sizes
+ * as the inputs; out-of-place only.  codes [E,N,K/2] (FP8 [E,N,K]); scales
+ * ignored (may be NULL) for FP8.  N % 16 == 0, K % 128 == 0.
+ */
+int fp4_weight_preshuffle(int wfmt, int E, int N, int K, const uint8_t* codes,
+                          const uint8_t* scales, uint8_t* codes_out, uint8_t* scales_out,
+                          void* stream);
 
 /*
  * moe_combine -- weighted top-k combine.

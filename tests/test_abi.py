@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
               "moe_combine", "mxfp4_to_fp8_channel"]:
         assert n in names
@@ -77,12 +77,12 @@ def test_quant_and_convert_reject_bad_K():
 def test_gemm_rejects_unsupported_combinations():
     def run(**kw):
         a = dict(stage=1, wfmt=0, afmt=0, n_experts=4, N=256, K=256, max_rows=8, max_tiles=4,
-                 block_m=16, gather_div=1, lda=256, ldo=128)
+                 block_m=16, gather_div=1, lda=256, ldo=128, w_layout=0)
         a.update(kw)
         args = fm.GemmArgs(a["stage"], a["wfmt"], a["afmt"], a["n_experts"], a["N"], a["K"],
                            a["max_rows"], a["max_tiles"], a["block_m"], a["gather_div"],
                            None, None, None, None, None, None, a["lda"], None, None, None, None,
-                           None, a["ldo"], None)
+                           None, a["ldo"], None, a.get("w_layout", 0))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -93,4 +93,16 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(wfmt=2, afmt=1, block_m=128)[0] == 1
     assert run(afmt=1, block_m=16)[0] == 1
     assert run(N=96)[0] == 1
+    assert run(w_layout=2)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
+
+
+def test_preshuffle_rejects_bad_shapes():
+    st, msg = _status(lambda lib: lib.fp4_weight_preshuffle(0, 2, 24, 256, None, None, None,
+                                                             None, None))
+    assert st == 1 and "N" in msg
+    st, msg = _status(lambda lib: lib.fp4_weight_preshuffle(0, 2, 32, 192, None, None, None,
+                                                             None, None))
+    assert st == 1
+    assert _status(lambda lib: lib.fp4_weight_preshuffle(0, 0, 32, 256, None, None, None, None,
+                                                          None))[0] == 0

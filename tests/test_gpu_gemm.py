@@ -65,7 +65,7 @@ def routing(rng, T, topk, E, skew=False):
 
 
 def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
-              exact=False):
+              exact=False, layout=0):
     rng = np.random.default_rng(seed)
     Et = E + ns
     k = topk + ns
@@ -110,9 +110,15 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
     n_out = N // 2 if stage == 1 else N
     out_f32 = torch.full((T * k, n_out), float("nan"), dtype=torch.float32, device="cuda")
     afmt_code = a_kw.pop("afmt")
+    wkw = gpu_weight_args(wd, wfmt)
+    if layout == gpu_lib.LAYOUT_FRAGMENT:
+        c, sc = gpu_lib.fp4_weight_preshuffle(gpu_lib.WFMT[wfmt], wkw["w"], wkw["w_scale"])
+        wkw["w"] = c
+        if wfmt != "fp8":
+            wkw["w_scale"] = sc
     out = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.WFMT[wfmt], afmt_code,
-                                   perm=perm, block_m=bm, out_f32=out_f32,
-                                   **gpu_weight_args(wd, wfmt), **a_kw, **gather)
+                                   perm=perm, block_m=bm, out_f32=out_f32, w_layout=layout,
+                                   **wkw, **a_kw, **gather)
     ref_unrounded = OG.grouped_stage(stage, a_sorted, perm_ref["expert_offsets"],
                                      lambda e: oracle_weight(wd, wfmt, e), rounding=False)
     g_bits = bits_of(out)[:n_rows]
@@ -142,10 +148,11 @@ DQ_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("case", DQ_CASES)
-def test_dq_gemm_parity(gpu_lib, case):
+def test_dq_gemm_parity(gpu_lib, case, layout):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
-    run_stage(gpu_lib, stage, wfmt, "bf16", T, topk, E, ns, H, I, bm, seed, skew)
+    run_stage(gpu_lib, stage, wfmt, "bf16", T, topk, E, ns, H, I, bm, seed, skew, layout=layout)
 
 
 MX_CASES = [
@@ -163,16 +170,60 @@ MX_CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("case", MX_CASES)
-def test_mx_gemm_parity(gpu_lib, case):
+def test_mx_gemm_parity(gpu_lib, case, layout):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
-    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew)
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew, layout=layout)
 
 
-@pytest.mark.parametrize("afmt,bm", [("bf16", 16), ("bf16", 64), ("mx", 64), ("mx", 256)])
-def test_gemm_exact_special_case(gpu_lib, afmt, bm):
+@pytest.mark.parametrize("afmt,bm,layout", [("bf16", 16, 0), ("bf16", 64, 1), ("mx", 64, 0),
+                                            ("mx", 256, 1)])
+def test_gemm_exact_special_case(gpu_lib, afmt, bm, layout):
     """E8M0 = 127 weights and activations in {0, +-.5, +-1, +-1.5, +-2}: every
     product is a multiple of 0.25 below 12, every partial sum of K <= 4096 terms
     stays below 2^22 in quarter units, so the float32 stage-2 result is exact in
     any summation order and must equal the oracle bit for bit."""
-    run_stage(gpu_lib, 2, "mx", afmt, 40, 2, 6, 1, 512, 2048, bm, 31, exact=True)
+    run_stage(gpu_lib, 2, "mx", afmt, 40, 2, 6, 1, 512, 2048, bm, 31, exact=True, layout=layout)
+
+
+def _fragment_reference(codes, scales, wfmt):
+    """Independent index-formula reference of the fragment-major layout."""
+    E, N = codes.shape[:2]
+    G = N // 16
+    if wfmt == "fp8":
+        K = codes.shape[2]
+        C = K // 128
+        e, n, k = np.meshgrid(np.arange(E), np.arange(N), np.arange(K), indexing="ij")
+        lane = n % 16 + 16 * ((k % 128) // 32)
+        f = (e * G + n // 16) * C + k // 128
+        out = np.empty(codes.size, np.uint8)
+        out[(f * 2048 + ((k % 32) // 16) * 1024 + lane * 16 + k % 16).ravel()] = codes.ravel()
+        return out.reshape(codes.shape), None
+    K = codes.shape[2] * 2
+    C = K // 128
+    e, n, kb = np.meshgrid(np.arange(E), np.arange(N), np.arange(K // 2), indexing="ij")
+    lane = n % 16 + 16 * ((kb % 64) // 16)
+    f = (e * G + n // 16) * C + kb // 64
+    oc = np.empty(codes.size, np.uint8)
+    oc[(f * 1024 + lane * 16 + kb % 16).ravel()] = codes.ravel()
+    per = 1 if wfmt == "mx" else 2
+    e, n, sb = np.meshgrid(np.arange(E), np.arange(N), np.arange(K // 32 * per), indexing="ij")
+    blk = sb // per
+    lane = n % 16 + 16 * (blk % 4)
+    f = (e * G + n // 16) * C + blk // 4
+    os_ = np.empty(scales.size, np.uint8)
+    os_[(f * 64 * per + lane * per + sb % per).ravel()] = scales.ravel()
+    return oc.reshape(codes.shape), os_.reshape(scales.shape)
+
+
+@pytest.mark.parametrize("wfmt", ["mx", "nvfp4", "fp8"])
+def test_preshuffle_layout(gpu_lib, wfmt):
+    rng = np.random.default_rng(40)
+    wd = make_weights(rng, 3, 48, 384, wfmt)
+    codes_ref, scales_ref = _fragment_reference(wd["codes"], wd["scale"], wfmt)
+    c, sc = gpu_lib.fp4_weight_preshuffle(gpu_lib.WFMT[wfmt], dev(wd["codes"]),
+                                          None if wfmt == "fp8" else dev(wd["scale"]))
+    assert np.array_equal(host(c), codes_ref)
+    if wfmt != "fp8":
+        assert np.array_equal(host(sc), scales_ref)

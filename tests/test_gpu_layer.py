@@ -89,7 +89,7 @@ def build_weights(w, experts, wfmt, torch_empty_experts):
     return np_w, dev_w
 
 
-def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, full_width=True):
+def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, fragment=True):
     logits = synth.router_logits(w, T, seed)
     bias = synth.router_bias(w)
     xb = synth.activations(w, T, seed)
@@ -98,7 +98,7 @@ def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, full_width=True):
     np_w, dev_w = build_weights(w, experts, wfmt, torch_empty_experts=True)
     cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                               topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
-                              block_m=block_m)
+                              block_m=block_m, fragment_layout=fragment)
     layer = gpu_lib.MoELayer(cfg, dev_w)
     b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
     ref = OL.moe_layer(xb, logits, bias, np_w, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
@@ -116,6 +116,10 @@ def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, full_width=True):
 
 def test_layer_tiny_bf16_path(gpu_lib):
     run_layer(gpu_lib, synth.WORKLOADS["tiny"], 16, "bf16", "mx", 16)
+
+
+def test_layer_tiny_bf16_path_rowmajor(gpu_lib):
+    run_layer(gpu_lib, synth.WORKLOADS["tiny"], 16, "bf16", "mx", 16, fragment=False)
 
 
 def test_layer_tiny_mx_path(gpu_lib):
