@@ -23,16 +23,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int p = pair_pos[t * k + j];
-    if (p < 0) continue;
-    const float w = (j < topk) ? topk_w[t * topk + j] : 1.f;
-    const uint4 v = *reinterpret_cast<const uint4*>(y + (int64_t)p * H + col);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  // Slots in batches of 8: all row loads of a batch are issued before the
+  // batch is accumulated, in ascending slot order.
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    uint4 v[8];
+    float w[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(w, bf16_to_f32(u[i] & 0xffffu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(w, bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj;
+      const int p = (j < k) ? pair_pos[t * k + j] : -1;
+      w[jj] = (p < 0) ? 0.f : ((j < topk) ? topk_w[t * topk + j] : 1.f);
+      v[jj] = (p < 0) ? make_uint4(0, 0, 0, 0)
+                      : *reinterpret_cast<const uint4*>(y + (int64_t)p * H + col);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (j0 + jj >= k) break;
+      const uint32_t u[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(w[jj], bf16_to_f32(u[i] & 0xffffu), acc[2 * i]);
+        acc[2 * i + 1] = fmaf(w[jj], bf16_to_f32(u[i] >> 16), acc[2 * i + 1]);
+      }
     }
   }
   uint32_t o[4];

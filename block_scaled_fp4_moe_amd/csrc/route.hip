@@ -2,11 +2,17 @@
 //
 // [GAUDI] "What was built": grouped top-k routing, sigmoid scoring with a
 // correction bias, for a DeepSeek-V3-style tower with 384 routed experts.
-// One 64-lane wavefront routes one token.  Lane l owns experts l, l+64, ...;
-// every selection decision compares float32 keys with index tie-breaks, so
-// the ids are bit-exact functions of the float32 scores.
+//
+// One 64-lane wavefront routes one token.  Lane l owns the contiguous experts
+// [l*P, l*P + P), P = ceil(E/64), so with E/n_group a multiple of P a group
+// is a run of adjacent lanes and its score (sum of the two largest keys) is a
+// short xor butterfly.  Each of the topk selection rounds is a wavefront
+// maximum of an order-preserving integer image of the float32 key, computed
+// with DPP row shifts and row broadcasts, then a ballot: the lowest lane
+// holding the maximum owns the lowest expert id among equal keys.  Every
+// decision compares float32 values, so the ids are bit-exact functions of the
+// float32 scores.
 #include <float.h>
-#include <limits.h>
 
 #include "common.h"
 
@@ -14,14 +20,39 @@ namespace fp4moe {
 
 constexpr int kRouteMaxPerLane = 16;   // E <= 1024
 
-struct Cand {
-  float key;
-  float s;
-  int idx;
-};
+// float32 -> uint32 with the same order (finite inputs; +0 and -0 differ,
+// but a key s + bias with s > 0 is never -0).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
-__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
-  return ka > kb || (ka == kb && ia < ib);
+// max(v, lane-shifted v) with DPP; lanes without a source keep v.
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t v) {
+  const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, BANK_MASK, false);
+  return v > t ? v : t;
+}
+
+// Maximum over the wavefront, returned to every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step<0x111, 0xf, 0xf>(v);   // row_shr:1
+  v = dpp_max_step<0x112, 0xf, 0xf>(v);   // row_shr:2  -> lanes hold max of 4
+  v = dpp_max_step<0x114, 0xf, 0xe>(v);   // row_shr:4  -> max of 8
+  v = dpp_max_step<0x118, 0xf, 0xc>(v);   // row_shr:8  -> lane 15 of a row: row max
+  v = dpp_max_step<0x142, 0xa, 0xf>(v);   // row_bcast:15 -> rows 1, 3 include rows 0, 2
+  v = dpp_max_step<0x143, 0xc, 0xf>(v);   // row_bcast:31 -> lane 63: wavefront max
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The two largest of {a1 >= a2} and {b1 >= b2}.
+__device__ __forceinline__ void merge_top2(float& a1, float& a2, float b1, float b2) {
+  if (a1 >= b1) {
+    a2 = fmaxf(a2, b1);
+  } else {
+    a2 = fmaxf(a1, b2);
+    a1 = b1;
+  }
 }
 
 __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits,
@@ -38,30 +69,61 @@ __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ log
   const int lane = threadIdx.x;
   const int64_t t = blockIdx.x;
   const float* row = logits + t * E;
+  const int P = (E + 63) / 64;
+  const int base = lane * P;
 
   float sv[kRouteMaxPerLane], kv[kRouteMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kRouteMaxPerLane; ++i) {
-    const int e = lane + 64 * i;
     sv[i] = 0.f;
     kv[i] = -FLT_MAX;
-    if (e < E) {
-      const double l = static_cast<double>(row[e]);
+    if (i < P && base + i < E) {
+      const double l = static_cast<double>(row[base + i]);
       const float s = static_cast<float>(1.0 / (1.0 + exp(-l)));   // one rounding to float32
-      const float b = bias ? bias[e] : 0.f;
-      const float key = __fadd_rn(s, b);
+      const float b = bias ? bias[base + i] : 0.f;
       sv[i] = s;
-      kv[i] = key;
-      s_key[e] = key;
+      kv[i] = __fadd_rn(s, b);
     }
   }
-  __syncthreads();
 
-  // Group stage: lane g scores group g by the sum of its two largest keys.
-  uint64_t kept = ~0ull;
-  int G = E;
-  if (n_group > 1) {
-    G = E / n_group;
+  // ---- group stage: which experts may be selected
+  bool lane_kept = true;                 // aligned case: whole lane kept or not
+  uint64_t kept_groups = ~0ull;          // fallback case: bit per group
+  const int G = E / n_group;
+  const bool aligned = n_group > 1 && (G % P) == 0 && __builtin_popcount(G / P) == 1 &&
+                       (G / P) * n_group <= 64;
+  if (n_group > 1 && aligned) {
+    const int L = G / P;                 // lanes per group, a power of two
+    float t1 = -FLT_MAX, t2 = -FLT_MAX;
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i) {
+      if (i < P && base + i < E) {
+        const float k = kv[i];
+        if (k > t1) {
+          t2 = t1;
+          t1 = k;
+        } else if (k > t2) {
+          t2 = k;
+        }
+      }
+    }
+    for (int off = 1; off < L; off <<= 1) {
+      const float o1 = __shfl_xor(t1, off, 64), o2 = __shfl_xor(t2, off, 64);
+      merge_top2(t1, t2, o1, o2);
+    }
+    const float gs = __fadd_rn(t1, t2);
+    const int mine = lane / L;
+    int rank = 0;
+    for (int g = 0; g < n_group; ++g) {
+      const float o = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gs), g * L));
+      rank += (o > gs || (o == gs && g < mine)) ? 1 : 0;
+    }
+    lane_kept = (mine < n_group) && rank < topk_group;
+  } else if (n_group > 1) {
+#pragma unroll
+    for (int i = 0; i < kRouteMaxPerLane; ++i)
+      if (i < P && base + i < E) s_key[base + i] = kv[i];
+    __syncthreads();
     float gs = -FLT_MAX;
     if (lane < n_group) {
       float t1 = -FLT_MAX, t2 = -FLT_MAX;
@@ -87,42 +149,39 @@ __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ log
       }
       keep = rank < topk_group;
     }
-    kept = __ballot(keep);
+    kept_groups = __ballot(keep);
   }
 
-  // Expert stage: topk rounds of a wavefront arg-max over the allowed experts.
-  uint32_t taken = 0;
+  // ---- selection: topk rounds of a wavefront arg-max
+  uint32_t avail = 0;                    // bit i: expert base+i is a candidate
+#pragma unroll
+  for (int i = 0; i < kRouteMaxPerLane; ++i) {
+    const int e = base + i;
+    const bool ok = i < P && e < E && lane_kept && ((kept_groups >> (e / G)) & 1ull);
+    avail |= (ok ? 1u : 0u) << i;
+  }
   for (int j = 0; j < topk; ++j) {
-    float bk = -FLT_MAX, bs = 0.f;
-    int bi = INT_MAX;
-    bool have = false;
+    uint32_t best = 0;
+    int bi = -1;
 #pragma unroll
     for (int i = 0; i < kRouteMaxPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && ((kept >> (e / G)) & 1ull)) {
-        if (!have || kv[i] > bk) {   // ascending e: strict > keeps the lower id on ties
-          bk = kv[i];
-          bs = sv[i];
-          bi = e;
-          have = true;
-        }
+      const uint32_t ok = order_key(kv[i]);
+      if (((avail >> i) & 1u) && ok > best) {   // ascending i: strict > keeps the lower id
+        best = ok;
+        bi = i;
       }
     }
+    const uint32_t gmax = wave_max_u32(best);
+    const uint64_t win = __ballot(bi >= 0 && best == gmax);
+    const int wl = __ffsll((unsigned long long)win) - 1;
+    float ws = 0.f;
+    if (lane == wl) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off, 64);
-      const float os = __shfl_xor(bs, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (better(ok, oi, bk, bi)) {
-        bk = ok;
-        bs = os;
-        bi = oi;
-      }
-    }
-    if (bi != INT_MAX && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == 0) {
-      s_sel_idx[j] = bi;
-      s_sel_s[j] = bs;
+      for (int i = 0; i < kRouteMaxPerLane; ++i)
+        if (i == bi) ws = sv[i];
+      avail &= ~(1u << bi);
+      s_sel_idx[j] = base + bi;
+      s_sel_s[j] = ws;
     }
   }
   __syncthreads();
