@@ -9,11 +9,13 @@
 // one contiguous KiB (2 KiB for FP8) and every scale load one contiguous run.
 //
 // Layouts (G = N/16 row groups, C = K/128 chunks, f = (e*G + n/16)*C + k/128,
-// lane = n%16 + 16*((k%128)/32)):
+// h = (e*C + k/128)*G + n/16, lane = n%16 + 16*((k%128)/32)):
 //   FP4 codes   byte f*1024 + lane*16 + (k%32)/2     (nibble k%2)
 //   FP8 codes   byte f*2048 + ((k%32)/16)*1024 + lane*16 + k%16
-//   E8M0 scale  byte f*64 + lane                      (block k/32)
-//   E4M3 scale  byte f*128 + lane*2 + (k%32)/16       (block k/16)
+//   E8M0 scale  byte h*64 + lane                      (block k/32)
+//   E4M3 scale  byte h*128 + lane*2 + (k%32)/16       (block k/16)
+// Codes are group-major (a group's chunks follow each other); scales are
+// chunk-major, so one chunk's scales of consecutive row groups are one run.
 // FP8 channel scales keep their [E, N] layout.
 #include "common.h"
 
@@ -54,13 +56,13 @@ __global__ __launch_bounds__(256) void shuffle_scales_kernel(const uint8_t* __re
   const int64_t row_bytes = (int64_t)(K / 32) * per_block;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t f = i / per_frag;
-    const int j = (int)(i - f * per_frag);
+    const int64_t h = i / per_frag;                 // (e*C + c)*G + grp
+    const int j = (int)(i - h * per_frag);
     const int lane = j / per_block, sub = j % per_block;
-    const int c = (int)(f % C);
-    const int64_t eg = f / C;
-    const int grp = (int)(eg % G);
-    const int64_t e = eg / G;
+    const int grp = (int)(h % G);
+    const int64_t ec = h / G;
+    const int c = (int)(ec % C);
+    const int64_t e = ec / C;
     const int n = grp * 16 + (lane & 15);
     const int blk = c * 4 + (lane >> 4);
     out[i] = in[(e * N + n) * row_bytes + (int64_t)blk * per_block + sub];

@@ -209,12 +209,13 @@ int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);
  * [ATOM] "Stage C: MXFP4 Linear GEMM": the production FP4 GEMMs take their
  * weight operand pre-shuffled for the matrix instruction; this layout is our
  * own, derived from the MFMA operand layout of our kernels.
- * With G = N/16 row groups, C = K/128 chunks, f = (e*G + n/16)*C + k/128 and
- * lane = n%16 + 16*((k%128)/32), element (e, n, k) goes to
+ * With G = N/16 row groups, C = K/128 chunks, f = (e*G + n/16)*C + k/128,
+ * h = (e*C + k/128)*G + n/16 and lane = n%16 + 16*((k%128)/32), element
+ * (e, n, k) goes to
  *   FP4 codes   byte f*1024 + lane*16 + (k%32)/2   (same nibble as before)
  *   FP8 codes   byte f*2048 + ((k%32)/16)*1024 + lane*16 + k%16
- *   E8M0 scale  byte f*64 + lane                     (MXFP4, per 32 along k)
- *   E4M3 scale  byte f*128 + lane*2 + (k%32)/16      (NVFP4, per 16 along k)
+ *   E8M0 scale  byte h*64 + lane                     (MXFP4, per 32 along k)
+ *   E4M3 scale  byte h*128 + lane*2 + (k%32)/16      (NVFP4, per 16 along k)
  * FP8 channel scales and NVFP4 tensor scales keep their layout.  Same sizes
  * as the inputs; out-of-place only.  codes [E,N,K/2] (FP8 [E,N,K]); scales
  * ignored (may be NULL) for FP8.  N % 16 == 0, K % 128 == 0.

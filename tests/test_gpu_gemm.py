@@ -211,9 +211,9 @@ def _fragment_reference(codes, scales, wfmt):
     e, n, sb = np.meshgrid(np.arange(E), np.arange(N), np.arange(K // 32 * per), indexing="ij")
     blk = sb // per
     lane = n % 16 + 16 * (blk % 4)
-    f = (e * G + n // 16) * C + blk // 4
+    h = (e * C + blk // 4) * G + n // 16          # scales: chunk-major
     os_ = np.empty(scales.size, np.uint8)
-    os_[(f * 64 * per + lane * per + sb % per).ravel()] = scales.ravel()
+    os_[(h * 64 * per + lane * per + sb % per).ravel()] = scales.ravel()
     return oc.reshape(codes.shape), os_.reshape(scales.shape)
 
 
