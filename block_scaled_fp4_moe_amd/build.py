@@ -3,6 +3,7 @@
     python -m block_scaled_fp4_moe_amd.build
 """
 
+import concurrent.futures
 import glob
 import os
 import subprocess
@@ -17,7 +18,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     # no packed-FP32 VALU ops in device code
@@ -30,16 +30,37 @@ def sources():
 
 
 def build(verbose=False):
+    """Compile every source to an object (in parallel), then link the library."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [hipcc] + HIPCC_FLAGS + inc + ["-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, r
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        results = list(ex.map(compile_one, srcs))
+    failed = [(o, r) for o, r in results if r.returncode != 0]
+    for _, r in results:
+        if r.stdout or r.stderr:
+            sys.stderr.write(r.stdout + r.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed on " + ", ".join(os.path.basename(o) for o, _ in failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc] + HIPCC_FLAGS + ["-I", os.path.join(ROOT, "include"),
-                                   "-I", os.path.join(HERE, "csrc")] + sources() + ["-o", tmp]
+    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for o, _ in results] + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libfp4moe.so")
+        raise RuntimeError("hipcc failed linking libfp4moe.so")
     os.replace(tmp, LIB)
     return LIB
 

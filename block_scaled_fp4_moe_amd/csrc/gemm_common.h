@@ -1,0 +1,135 @@
+// fp4_grouped_gemm: one expert-grouped GEMM stage of the MoE layer on gfx950.
+//
+// [ATOM] "Stage D: MXFP4 Fused MoE": two stages, stage 1 on the fused gate/up
+// weights, stage 2 on the down weights.  [ATOM] "When Is the Scale Applied?":
+// for bf16 activations the block scale is absorbed while decoding the weight
+// before a bf16 MFMA; for FP4 activations the payloads and E8M0 scales go
+// straight into the gfx950 scaled MFMA.  [NVFP4] "Memory Management": the MoE
+// path fuses dequantization into the GEMM tile, no bf16 weight buffer is
+// staged in memory.  [GAUDI] "What was built": gate and up rows are
+// concatenated in one fused tensor (gate first, by our reading).
+//
+// Operand layout (both MFMA families): in a 16x16 MFMA tile lane l holds one
+// 32-element MX block of row (l % 16), block index (l / 16) of the current
+// 128-wide K chunk.  In the natural row-major [N, K/2] layout that is exactly
+// one aligned 16-byte load per lane, with the four lanes of a row reading 64
+// contiguous bytes, and its scale is one byte -- no shuffling and no LDS for
+// the weights.  The accumulator of lane l holds rows 4*(l/16)..+3 (tokens) of
+// column l % 16 (weight row).
+//
+// Families
+//   dq  (wfmt MXFP4 | NVFP4 | FP8; afmt BF16, or MXFP4 with FP8 weights):
+//       both operands are brought to bf16 in registers (v_cvt_scalef32_pk_*),
+//       then v_mfma_f32_16x16x32_bf16 with float32 accumulation.  The decode is
+//       exact: E2M1 x E8M0, E2M1 x E4M3 and E4M3 values all fit bf16.  A
+//       workgroup is four waves that split the K chunks round-robin and reduce
+//       through LDS, so even a single decode token spreads an expert over many
+//       CUs.  FP8 weights carry a per-row float channel scale applied in the
+//       epilogue.
+//   mx  (afmt MXFP4; wfmt MXFP4): v_mfma_scale_f32_16x16x128_f8f6f4 FP4 x FP4
+//       with the E8M0 bytes as the scale operands.
+//
+// FP8 weights with MXFP4 activations go through the bf16 path on purpose: in
+// the mixed FP4 x FP8 form of the scaled MFMA each FP4 lane holds halves of
+// two different 32-element K blocks, so one E8M0 scale per lane cannot carry
+#pragma once
+
+#include "common.h"
+
+namespace fp4moe {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+struct GemmParams {
+  int N, K, n_experts, block_m, gather_div, w_layout;
+  int64_t lda, ldo;
+  const uint8_t* w;
+  const uint8_t* w_scale;
+  const float* w_tensor_scale;
+  const float* w_channel_scale;
+  const void* a;
+  const uint8_t* a_scale;
+  const int32_t* gather;
+  const int32_t* offsets;
+  const int32_t* tiles;
+  const int32_t* n_tiles;
+  uint16_t* out;
+  float* out_f32;
+};
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+__device__ __forceinline__ v8bf cat8(v2bf a, v2bf b, v2bf c, v2bf d) {
+  const v4bf lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+  const v4bf hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// E4M3FN byte -> float (finite codes).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// Eight bf16 weights (elements 8s..8s+7 of the lane's block) from dword `d`
+// of the 16-byte E2M1 payload, times an E8M0 scale given as float.
+__device__ __forceinline__ v8bf decode_mx8(uint32_t d, float scale) {
+  return cat8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3));
+}
+
+// Same for NVFP4: E2M1 times an arbitrary E4M3 scale.  The product has at
+// most 6 significant bits, so it is exact in bf16.
+__device__ __forceinline__ v2bf nv_pair(uint32_t d, float scale, int sel) {
+  v2f f;
+  switch (sel) {
+    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2); break;
+    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3); break;
+  }
+  v2bf r;
+  r[0] = (__bf16)(f[0] * scale);
+  r[1] = (__bf16)(f[1] * scale);
+  return r;
+}
+
+__device__ __forceinline__ v8bf decode_nv8(uint32_t d, float scale) {
+  return cat8(nv_pair(d, scale, 0), nv_pair(d, scale, 1), nv_pair(d, scale, 2),
+              nv_pair(d, scale, 3));
+}
+
+// Eight bf16 weights from two dwords of E4M3 codes (exact).
+__device__ __forceinline__ v8bf decode_fp8x8(uint32_t d0, uint32_t d1) {
+  return cat8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false),
+              __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
+
+// Workgroups that fill the device: 8 per compute unit (queried once).
+int grid_cap();
+
+// Family launchers (formats, block_m and shapes already validated).
+void launch_dq_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
+                    hipStream_t s);
+void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+
+}  // namespace fp4moe
