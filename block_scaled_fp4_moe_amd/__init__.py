@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(HERE, "libfp4moe.so")
 W_MXFP4, W_NVFP4, W_FP8 = 0, 1, 2
 A_BF16, A_MXFP4 = 0, 1
 LAYOUT_ROWMAJOR, LAYOUT_FRAGMENT = 0, 1
+A_LAYOUT_ROWMAJOR, A_LAYOUT_CHUNKED = 0, 1
 WFMT = {"mx": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8}
 
 _lib = None
@@ -44,7 +45,7 @@ class GemmArgs(ctypes.Structure):
         ("a_row_gather", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
         ("tiles", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_f32", ctypes.c_void_p),
-        ("w_layout", ctypes.c_int),
+        ("w_layout", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_int),
     ]
 
 
@@ -65,6 +66,7 @@ def load():
         "moe_permute_workspace": ([I, I, I, I, I], S),
         "moe_permute": ([P, I, I, I, I, I, P, S, P, P, P, P, P, P, P], I),
         "mxfp4_quant_1x32": ([P, I, I, I64, P, P, P, P, P], I),
+        "mxfp4_quant_1x32_chunked": ([P, I, I, I64, P, I, I, P, P, P, P], I),
         "nvfp4_qdq_workspace": ([], S),
         "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, S, P], I),
         "fp4_grouped_gemm": ([ctypes.POINTER(GemmArgs), P], I),
@@ -173,6 +175,26 @@ def mxfp4_quant_1x32(x, row_gather=None, row_count=None, codes=None, scales=None
     return codes, scales
 
 
+def mxfp4_quant_1x32_chunked(x, row_map=None, map_k=1, out_rows=None, row_count=None,
+                             codes=None, scales=None, stream=None):
+    """x bf16 [M, K] -> chunk-major (codes uint8 [K/128, out_rows, 64], scales [K/128, out_rows, 4]).
+
+    Input row r goes to output rows row_map[r*map_k + j] (j < map_k), or to row r."""
+    lib = load()
+    xs = _u16(x)
+    M, K = xs.shape
+    if out_rows is None:
+        out_rows = codes.shape[1] if codes is not None else (M * map_k if row_map is not None else M)
+    assert xs.stride(1) == 1
+    if codes is None:
+        codes = torch.empty((K // 128, out_rows, 64), dtype=torch.uint8, device=_dev(x))
+    if scales is None:
+        scales = torch.empty((K // 128, out_rows, 4), dtype=torch.uint8, device=_dev(x))
+    _check(lib.mxfp4_quant_1x32_chunked(_p(xs), M, K, xs.stride(0), _p(row_map), map_k, out_rows,
+                                        _p(row_count), _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
+
+
 def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=None,
               tensor_scale_out=None, workspace=None, stream=None):
     """x bf16 [M, K] -> y bf16 [M, K] (and optional codes, scales, tensor scale)."""
@@ -192,20 +214,27 @@ def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=N
 def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale=None,
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
                      gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
-                     stream=None):
+                     a_layout=0, stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
-    codes [rows, K/2] with a_scale [rows, K/32].  Returns out bf16 [max_rows, N_out]."""
+    codes [rows, K/2] with a_scale [rows, K/32] (a_layout 0), or chunk-major
+    MXFP4 codes [K/128, rows, 64] with a_scale [K/128, rows, 4] (a_layout 1).
+    Returns out bf16 [max_rows, N_out]."""
     lib = load()
     E, N = w.shape[0], w.shape[1]
     K = w.shape[2] if wfmt == W_FP8 else w.shape[2] * 2
     n_out = N // 2 if stage == 1 else N
     if max_rows is None:
         max_rows = perm["sorted_pairs"].shape[0]
+    a_rows = 0
     if afmt == A_BF16:
         a_ = _u16(a)
         lda = a_.stride(0)
+    elif a_layout == A_LAYOUT_CHUNKED:
+        a_ = a
+        a_rows = a.shape[1]
+        lda = K
     else:
         a_ = a
         lda = a.stride(0) * 2
@@ -219,7 +248,7 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     None if a_row_gather is None else a_row_gather.data_ptr(),
                     perm["expert_offsets"].data_ptr(), perm["tiles"].data_ptr(),
                     perm["n_tiles"].data_ptr(), out.data_ptr(), out.stride(0),
-                    None if out_f32 is None else out_f32.data_ptr(), w_layout)
+                    None if out_f32 is None else out_f32.data_ptr(), w_layout, a_layout, a_rows)
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
 

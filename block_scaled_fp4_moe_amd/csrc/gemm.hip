@@ -64,9 +64,19 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: w_layout=%d", a->w_layout);
   FP4MOE_REQUIRE(a->w_layout == FP4MOE_LAYOUT_ROWMAJOR || a->N % 16 == 0,
                  "fp4_grouped_gemm: fragment layout needs N %% 16 == 0");
+  FP4MOE_REQUIRE(a->a_layout == FP4MOE_A_LAYOUT_ROWMAJOR || a->a_layout == FP4MOE_A_LAYOUT_CHUNKED,
+                 "fp4_grouped_gemm: a_layout=%d", a->a_layout);
+  const bool a_chunked = a->a_layout == FP4MOE_A_LAYOUT_CHUNKED;
+  FP4MOE_REQUIRE(!a_chunked || (mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
+                                (a->block_m == 128 || a->block_m == 256)),
+                 "fp4_grouped_gemm: chunked activations need MXFP4 x MXFP4, fragment weights "
+                 "and block_m 128 or 256");
+  FP4MOE_REQUIRE(!a_chunked || (a->a_rows >= 1 && a->a_rows <= (1 << 26) &&
+                                (a->a_row_gather || a->a_rows >= a->max_rows)),
+                 "fp4_grouped_gemm: a_rows=%d (max_rows=%d)", a->a_rows, a->max_rows);
   const int n_out = a->stage == 1 ? a->N / 2 : a->N;
   FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
-  FP4MOE_REQUIRE(a->lda >= a->K && a->lda % 32 == 0, "fp4_grouped_gemm: lda=%lld",
+  FP4MOE_REQUIRE(a_chunked || (a->lda >= a->K && a->lda % 32 == 0), "fp4_grouped_gemm: lda=%lld",
                  (long long)a->lda);
   if (a->max_tiles == 0 || a->max_rows == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(a->w && a->a && a->expert_offsets && a->tiles && a->n_tiles && a->out,
@@ -89,6 +99,8 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.block_m = a->block_m;
   p.gather_div = a->gather_div;
   p.w_layout = a->w_layout;
+  p.a_layout = a->a_layout;
+  p.a_rows = a->a_rows;
   p.lda = a->lda;
   p.ldo = a->ldo;
   p.w = a->w;

@@ -40,6 +40,7 @@ namespace fp4moe {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -47,7 +48,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 struct GemmParams {
-  int N, K, n_experts, block_m, gather_div, w_layout;
+  int N, K, n_experts, block_m, gather_div, w_layout, a_layout, a_rows;
   int64_t lda, ldo;
   const uint8_t* w;
   const uint8_t* w_scale;

@@ -387,26 +387,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maximum) as a builtin,
+// so that the compiler's own wait insertion knows the LDS reads are complete.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int STAGE, int WM>
-__global__ __launch_bounds__(256, 1) void mx_dma_gemm_kernel(GemmParams p) {
-  constexpr int S = 4;                              // pipeline stages
-  constexpr int BM = 32 * WM;
-  constexpr int WN = 8;
+// Wait until at most `newer` chunks (D DMA instructions each) issued after the
+// current one are still in flight.
+template <int D, int SM2>
+__device__ __forceinline__ void wait_chunks(int newer) {
+  if (SM2 >= 4 && newer >= 4) wait_vmcnt<(SM2 >= 4 ? 4 : 0) * D>();
+  else if (SM2 >= 3 && newer == 3) wait_vmcnt<(SM2 >= 3 ? 3 : 0) * D>();
+  else if (SM2 >= 2 && newer == 2) wait_vmcnt<(SM2 >= 2 ? 2 : 0) * D>();
+  else if (newer == 1) wait_vmcnt<D>();
+  else wait_vmcnt<0>();
+}
+
+// WAVES_M x WAVES_N waves (4 in all); each wave owns WM M blocks x 8 weight
+// groups of 16 rows (a 16*WM x 128 sub-tile, 32 MFMA tiles).  The
+// workgroup tile is BM = 16*WM*WAVES_M rows by 128*WAVES_N weight rows.
+//   WAVES_M = 2 (block_m 128): 128 x 256, two M tiles of an expert share a
+//     weight slice through L2;
+//   WAVES_M = 4 (block_m 256): 256 x 128, one workgroup covers every row of
+//     a typical routed expert, so each weight byte is fetched from HBM once
+//     whatever the timing of other workgroups; the activation chunk
+//     (16 KiB) is what the workgroups of one XCD share through L2.
+template <int STAGE, int WM, int WAVES_M, int WAVES_N, int S>
+__global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void mx_dma_gemm_kernel(GemmParams p) {
+  constexpr int NW = WAVES_M * WAVES_N;             // waves per workgroup
+  constexpr int BM = 16 * WM * WAVES_M;
+  constexpr int WN = 8;                             // weight groups per wave
+  constexpr int NG_WG = WN * WAVES_N;               // weight groups per workgroup
+  constexpr int GPW = NG_WG / NW;                   // weight groups copied per wave
   constexpr int MBLK = BM / 16;                     // M blocks per tile
-  constexpr int A_MB_PER_WAVE = MBLK / 4;
+  constexpr int AMPW = MBLK / NW;                   // A blocks copied per wave
   constexpr int OUT_PER_WAVE = (STAGE == 1) ? (WN / 2) * 16 : WN * 16;
-  constexpr int OUT_PER_WG = 2 * OUT_PER_WAVE;
+  constexpr int OUT_PER_WG = WAVES_N * OUT_PER_WAVE;
   constexpr int OFF_AS = BM * 64;                   // A codes: [MBLK][64 lanes][16 B]
   constexpr int OFF_B = OFF_AS + BM * 4;            // A scales: [row][4 blocks]
-  constexpr int OFF_BS = OFF_B + 16 * 1024;         // B codes: [16 groups][64 lanes][16 B]
-  constexpr int STAGE_BYTES = OFF_BS + 16 * 64;     // B scales: [16 groups][64 lanes]
-  constexpr int D = A_MB_PER_WAVE + 1 + 4 + 1;      // DMA instructions per wave per chunk
+  constexpr int OFF_BS = OFF_B + NG_WG * 1024;      // B codes: [NG_WG groups][64 lanes][16 B]
+  constexpr int STAGE_BYTES = OFF_BS + NW * 256;    // B scales: [NW waves][256 B]
+  constexpr int D = AMPW + 1 + GPW + 1;             // DMA instructions per wave per chunk
   static_assert(D * (S - 2) <= 63, "vmcnt range");
+  static_assert(S >= 3 && S <= 6, "ring depth");
+  static_assert(S * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(BM / 64 >= 1 && BM % 64 == 0 && NW >= BM / 64, "A scale copy: one dword per row");
+  static_assert(GPW >= 1 && GPW <= 4 && AMPW >= 1, "copy split");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int g = lane >> 4, r16 = lane & 15;
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int n_nb = n_out / OUT_PER_WG;
@@ -414,7 +444,12 @@ __global__ __launch_bounds__(256, 1) void mx_dma_gemm_kernel(GemmParams p) {
   const int G = p.N / 16;
   const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
   const uint8_t* A = static_cast<const uint8_t*>(p.a);
-  const int64_t a_row_bytes = p.lda / 2, a_srow = p.lda / 32;
+  // row-major A: row stride lda/2 (scales lda/32), next chunk +64 (+4);
+  // chunk-major A: row stride 64 (4), next chunk one slab of a_rows rows
+  const bool chunked = p.a_layout == FP4MOE_A_LAYOUT_CHUNKED;
+  const int64_t a_row_bytes = chunked ? 64 : p.lda / 2, a_srow = chunked ? 4 : p.lda / 32;
+  const int64_t a_cstride = chunked ? (int64_t)p.a_rows * 64 : 64;
+  const int64_t as_cstride = chunked ? (int64_t)p.a_rows * 4 : 4;
   const uint32_t smem_base = lds_offset(smem);
 
   constexpr int NX = 8;
@@ -425,9 +460,8 @@ __global__ __launch_bounds__(256, 1) void mx_dma_gemm_kernel(GemmParams p) {
   const int64_t w_end = min(n_work, w_begin + per);
 
   for (int64_t wi = w_begin + slot; wi < w_end; wi += slots) {
-    // Items of one expert are ordered (column block, M tile): the M tiles that
-    // share a weight slice run side by side on one XCD, so the slice is read
-    // from HBM once and from L2 for the other tiles.
+    // Items of one expert are ordered (column block, M tile): M tiles that
+    // share a weight slice run side by side on one XCD.
     const int any_tile = (int)(wi / n_nb);
     const int e = p.tiles[2 * any_tile];
     const int t0 = any_tile - p.tiles[2 * any_tile + 1];
@@ -439,111 +473,199 @@ __global__ __launch_bounds__(256, 1) void mx_dma_gemm_kernel(GemmParams p) {
 
     // DMA sources of this wave: uniform 64-bit bases plus 32-bit lane offsets;
     // rows past the segment read row 0.
-    uint32_t a_off[A_MB_PER_WAVE];
+    uint32_t a_off[AMPW];
 #pragma unroll
-    for (int j = 0; j < A_MB_PER_WAVE; ++j) {
-      const int r = tile_row0 + (wave * A_MB_PER_WAVE + j) * 16 + r16;
+    for (int j = 0; j < AMPW; ++j) {
+      const int r = tile_row0 + (wave * AMPW + j) * 16 + r16;
       int64_t arow = 0;
       if (r < row_end) arow = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
       a_off[j] = (uint32_t)(arow * a_row_bytes) + g * 16;
     }
     uint32_t as_off;
     {
-      const int r = tile_row0 + (wave % (BM / 64)) * 64 + lane;   // BM=128: waves 2,3 repeat 0,1
+      // BM/64 dword copies cover the tile's rows; with BM = 128 waves 2, 3
+      // repeat the copies of waves 0, 1 (same bytes, same LDS slots)
+      const int r = tile_row0 + (wave % (BM / 64)) * 64 + lane;
       int64_t arow = 0;
       if (r < row_end) arow = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
       as_off = (uint32_t)(arow * a_srow);
     }
-    // the workgroup's 16 weight groups: stage 1 gate 0..7 then up 0..7;
-    // wave w copies groups 4w..4w+3 (one run of 4 for the scales)
-    const int grp0 = (STAGE == 1) ? ((wave < 2) ? nb * 8 + wave * 4 : G / 2 + nb * 8 + (wave - 2) * 4)
-                                  : nb * 16 + wave * 4;
+    // The workgroup's NG_WG weight groups in LDS order: stage 1 gate groups
+    // then the matching up groups.  Wave w copies LDS groups [w*GPW, +GPW),
+    // one contiguous run of groups in the weight tensor.
+    int grp0;
+    {
+      const int j0 = wave * GPW;
+      if (STAGE == 1)
+        grp0 = (j0 < NG_WG / 2) ? nb * (NG_WG / 2) + j0 : G / 2 + nb * (NG_WG / 2) + (j0 - NG_WG / 2);
+      else
+        grp0 = nb * NG_WG + j0;
+    }
     const uint8_t* b_base = p.w + ((int64_t)e * G + grp0) * nkc * 1024;
     const uint32_t b_lane = lane * 16;
+    // scales of the wave's GPW groups: GPW*64 bytes; lanes past that repeat
     const uint8_t* bs_base = p.w_scale + ((int64_t)e * nkc * G + grp0) * 64;
-    const uint32_t bs_lane = lane * 4;
-    const uint32_t lds_wave = smem_base + (uint32_t)(wave * 0);   // uniform base
+    const uint32_t bs_lane = (lane % (GPW * 16)) * 4;
 
-    auto issue = [&](int c) {
-      const uint32_t st = lds_wave + (uint32_t)((c % S) * STAGE_BYTES);
+    // copy chunk c into the ring stage of chunk slot q
+    auto issue = [&](int c, int q) {
+      const uint32_t st = smem_base + (uint32_t)((q % S) * STAGE_BYTES);
 #pragma unroll
-      for (int j = 0; j < A_MB_PER_WAVE; ++j)
-        dma_b128(A + a_off[j] + (int64_t)c * 64, st + (wave * A_MB_PER_WAVE + j) * 1024);
-      dma_b32(p.a_scale + as_off + c * 4, st + OFF_AS + (wave % (BM / 64)) * 256);
+      for (int j = 0; j < AMPW; ++j)
+        dma_b128(A + a_off[j] + (int64_t)c * a_cstride, st + (wave * AMPW + j) * 1024);
+      dma_b32(p.a_scale + as_off + (int64_t)c * as_cstride, st + OFF_AS + (wave % (BM / 64)) * 256);
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dma_b128(b_base + ((int64_t)q * nkc + c) * 1024 + b_lane, st + OFF_B + (wave * 4 + q) * 1024);
+      for (int q = 0; q < GPW; ++q)
+        dma_b128(b_base + ((int64_t)q * nkc + c) * 1024 + b_lane, st + OFF_B + (wave * GPW + q) * 1024);
       dma_b32(bs_base + (int64_t)c * G * 64 + bs_lane, st + OFF_BS + wave * 256);
     };
 
-    v4f acc[WM][WN];
+    // 32x32 output tiles: MT per wave in M, NT in N (32 weight rows each)
+    constexpr int MT = WM / 2, NT = WN / 2;
+    v16f acc[MT][NT];
 #pragma unroll
-    for (int mb = 0; mb < WM; ++mb)
+    for (int mt2 = 0; mt2 < MT; ++mt2)
 #pragma unroll
-      for (int nbk = 0; nbk < WN; ++nbk) acc[mb][nbk] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int c = 0; c < S - 1 && c < nkc; ++c) issue(c);
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mt2][nt][i] = 0.f;
 
     // per-lane LDS read bases within a stage; fragments sit at constant offsets
-    const int a_lds = wm * WM * 1024 + lane * 16;
-    const int as_lds = OFF_AS + wm * WM * 64 + r16 * 4 + g;
-    const int b_lds = OFF_B + ((STAGE == 1) ? wn * 4 : wn * 8) * 1024 + lane * 16;
-    const int bs_lds = OFF_BS + ((STAGE == 1) ? wn * 4 : wn * 8) * 64 + lane;
+    // The 32x32x64 MFMA takes, in lane l, row (or weight row) l % 32 and the
+    // 32-element block l / 32 of a 64-wide K step.  In the ring both operands
+    // sit as 16-row fragments (lane' = row % 16 + 16 * block of the 128-wide
+    // chunk), so lane l of K step h reads fragment (l % 32) / 16 at lane'
+    // l % 16 + 16 * (2h + l / 32): a per-lane base plus constant offsets.
+    const int m16 = (lane & 31) >> 4, kb = lane >> 5;
+    const int frag_lane = m16 * 1024 + (lane & 15) * 16 + kb * 256;
+    const int a_lds = wm * WM * 1024 + frag_lane;
+    const int as_lds = OFF_AS + wm * WM * 64 + (lane & 31) * 4 + kb;
+    const int b_lds = OFF_B + frag_lane;
+    const int bs_lds = OFF_BS + m16 * 64 + (lane & 15) + 16 * kb;
 
-    for (int c = 0; c < nkc; ++c) {
-      const int newer = min(S - 2, nkc - 1 - c);
-      if (newer >= 2) wait_vmcnt<2 * D>();
-      else if (newer == 1) wait_vmcnt<D>();
-      else wait_vmcnt<0>();
-      wg_barrier();
-      if (c + S - 1 < nkc) issue(c + S - 1);
-
+    // MFMA operands of one chunk (two 64-wide K steps), read from its ring
+    // stage into registers
+    v4u bo[2][NT], ao[2][MT];
+    int bso[2][NT], aso[2][MT];
+    auto read_ops = [&](int c) {
       const uint8_t* st = smem + (c % S) * STAGE_BYTES;
-      v8i bf[WN];
-      int bsc[WN];
 #pragma unroll
-      for (int nbk = 0; nbk < WN; ++nbk) {
-        // stage 1: gate blocks 0..3 at groups wn*4+q, up blocks at 8+wn*4+q
-        const int jo = (STAGE == 1) ? ((nbk < WN / 2) ? nbk : 8 + (nbk - WN / 2)) : nbk;
-        const uint4 v = *reinterpret_cast<const uint4*>(st + b_lds + jo * 1024);
-        bf[nbk] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        bsc[nbk] = st[bs_lds + jo * 64];
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          // first LDS group of the tile: stage 1 gate tiles then up tiles
+          const int ju = (STAGE == 1)
+                             ? ((nt < NT / 2) ? wn * (WN / 2) + nt * 2 : NG_WG / 2 + wn * (WN / 2) + (nt - NT / 2) * 2)
+                             : wn * WN + nt * 2;
+          bo[h][nt] = *reinterpret_cast<const v4u*>(st + b_lds + ju * 1024 + h * 512);
+          bso[h][nt] = st[bs_lds + (ju / GPW) * 256 + (ju % GPW) * 64 + h * 32];
+        }
+#pragma unroll
+        for (int mt2 = 0; mt2 < MT; ++mt2) {
+          ao[h][mt2] = *reinterpret_cast<const v4u*>(st + a_lds + mt2 * 2048 + h * 512);
+          aso[h][mt2] = st[as_lds + mt2 * 128 + 2 * h];
+        }
       }
+    };
+    auto mma = [&]() {
 #pragma unroll
-      for (int mb = 0; mb < WM; ++mb) {
-        const uint4 av = *reinterpret_cast<const uint4*>(st + a_lds + mb * 1024);
-        const int as = st[as_lds + mb * 64];
-        const v8i af = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int nbk = 0; nbk < WN; ++nbk)
-          acc[mb][nbk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              af, bf[nbk], acc[mb][nbk], 4, 4, 0, as, 0, bsc[nbk]);
+        for (int mt2 = 0; mt2 < MT; ++mt2) {
+          const v8i af = v8i{(int)ao[h][mt2][0], (int)ao[h][mt2][1], (int)ao[h][mt2][2], (int)ao[h][mt2][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const v8i bf = v8i{(int)bo[h][nt][0], (int)bo[h][nt][1], (int)bo[h][nt][2], (int)bo[h][nt][3], 0, 0, 0, 0};
+            acc[mt2][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[mt2][nt], 4, 4, 0,
+                                                                           aso[h][mt2], 0, bso[h][nt]);
+          }
+        }
+    };
+
+    // Chunk c is multiplied from stage c % S while the copies of chunks
+    // c+1 .. c+S-1 are in flight; the copy of chunk c+S-1 is issued right
+    // after the barrier that retires chunk c-1's stage.
+    for (int c = 0; c < S - 1 && c < nkc; ++c) issue(c, c);
+    if constexpr (NW == 8) {
+      // Ping-pong: the two waves of a SIMD (waves w and w+4) run half a
+      // chunk apart, so one multiplies while the other reads its operands
+      // from LDS.  All waves run the same loop; waves 4-7 start one barrier
+      // late and waves 0-3 end with one extra barrier.  With barriers
+      // numbered from 0, chunk c is read in half-step 2c by waves 0-3 and in
+      // half-step 2c+1 by waves 4-7, and multiplied one half-step later.
+      // Rules that keep the ring safe: every wave completes its LDS reads
+      // before each barrier; chunk c has landed (every wave's copies) before
+      // barrier 2c; the refill issued after a wave's first barrier of chunk
+      // c targets chunk c-1's stage, last read before barrier 2c.
+      const int grp = wave >> 2;
+      if (grp == 1) {
+        wait_chunks<D, S - 2>(min(S - 2, nkc - 1));
+        wg_barrier();
+      }
+      // The barriers take the accumulators (first) and the operands (second)
+      // as in/out register operands: the MFMAs of a chunk can then be moved
+      // neither before the second barrier nor past the next first barrier,
+      // which keeps each wave's multiply and read phases apart.
+      static_assert(MT == 2 && NT == 4, "pinned barrier operand lists");
+      for (int c = 0; c < nkc; ++c) {
+        wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));   // own copies of chunk c
+        wait_lgkm0();
+        asm volatile("s_barrier"
+                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                       "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3])
+                     :
+                     : "memory");
+        if (c + S - 1 < nkc) issue(c + S - 1, c + S - 1);
+        read_ops(c);
+        // waves 4-7 pass barrier 2c+2 next: their copies of chunk c+1 must be in
+        if (grp == 1 && c + 1 < nkc) wait_chunks<D, S - 2>(min(S - 2, nkc - 2 - c));
+        wait_lgkm0();
+        asm volatile("s_barrier"
+                     : "+v"(bo[0][0]), "+v"(bo[0][1]), "+v"(bo[0][2]), "+v"(bo[0][3]),
+                       "+v"(bo[1][0]), "+v"(bo[1][1]), "+v"(bo[1][2]), "+v"(bo[1][3]),
+                       "+v"(ao[0][0]), "+v"(ao[0][1]), "+v"(ao[1][0]), "+v"(ao[1][1]),
+                       "+v"(bso[0][0]), "+v"(bso[0][1]), "+v"(bso[0][2]), "+v"(bso[0][3]),
+                       "+v"(bso[1][0]), "+v"(bso[1][1]), "+v"(bso[1][2]), "+v"(bso[1][3]),
+                       "+v"(aso[0][0]), "+v"(aso[0][1]), "+v"(aso[1][0]), "+v"(aso[1][1])
+                     :
+                     : "memory");
+        mma();
+      }
+      if (grp == 0) wg_barrier();
+    } else {
+      for (int c = 0; c < nkc; ++c) {
+        wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));
+        wg_barrier();
+        if (c + S - 1 < nkc) issue(c + S - 1, c + S - 1);
+        read_ops(c);
+        mma();
       }
     }
     wg_barrier();   // every wave is done with the ring before the next item refills it
 
-    // epilogue
-    const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE;
-    const int wrow0 = tile_row0 + wm * WM * 16;
+    // epilogue: lane l holds column l % 32 of each 32x32 tile and rows
+    // (i / 4) * 8 + (l / 32) * 4 + i % 4 in accumulator element i
+    const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane & 31);
+    const int wrow0 = tile_row0 + wm * WM * 16 + kb * 4;
 #pragma unroll
-    for (int mb = 0; mb < WM; ++mb) {
+    for (int mt2 = 0; mt2 < MT; ++mt2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wrow0 + mb * 16 + g * 4 + i;
+      for (int i = 0; i < 16; ++i) {
+        const int r = wrow0 + mt2 * 32 + (i >> 2) * 8 + (i & 3);
         if (r >= row_end) continue;
         if (STAGE == 1) {
 #pragma unroll
-          for (int j = 0; j < WN / 2; ++j) {
-            const float h = silu_mul(acc[mb][j][i], acc[mb][j + WN / 2][i]);
-            const int64_t o = (int64_t)r * p.ldo + col0 + j * 16 + r16;
+          for (int j = 0; j < NT / 2; ++j) {
+            const float h = silu_mul(acc[mt2][j][i], acc[mt2][j + NT / 2][i]);
+            const int64_t o = (int64_t)r * p.ldo + col0 + j * 32;
             p.out[o] = (uint16_t)f32_to_bf16_rne(h);
             if (p.out_f32) p.out_f32[o] = h;
           }
         } else {
 #pragma unroll
-          for (int nbk = 0; nbk < WN; ++nbk) {
-            const float y = acc[mb][nbk][i];
-            const int64_t o = (int64_t)r * p.ldo + col0 + nbk * 16 + r16;
+          for (int nt = 0; nt < NT; ++nt) {
+            const float y = acc[mt2][nt][i];
+            const int64_t o = (int64_t)r * p.ldo + col0 + nt * 32;
             p.out[o] = (uint16_t)f32_to_bf16_rne(y);
             if (p.out_f32) p.out_f32[o] = y;
           }
@@ -575,14 +697,15 @@ static void launch_mx_lds(const GemmParams& p, int max_tiles, hipStream_t s) {
   hipLaunchKernelGGL((mx_lds_gemm_kernel<STAGE, WM>), dim3(grid), dim3(256), 0, s, p);
 }
 
-template <int STAGE, int WM>
+template <int STAGE, int WM, int WAVES_M, int WAVES_N, int S>
 static void launch_mx_dma(const GemmParams& p, int max_tiles, hipStream_t s) {
-  const int out_per_wg = (STAGE == 1) ? 128 : 256;
+  const int out_per_wg = ((STAGE == 1) ? 64 : 128) * WAVES_N;
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
   int cap = grid_cap() / 8;              // one workgroup (four waves) per CU
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((mx_dma_gemm_kernel<STAGE, WM>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((mx_dma_gemm_kernel<STAGE, WM, WAVES_M, WAVES_N, S>), dim3(grid),
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, p);
 }
 
 template <int STAGE>
@@ -592,10 +715,13 @@ static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
     case 32: launch_mx_wm<STAGE, 1>(p, max_tiles, s); break;
     case 64: launch_mx_wm<STAGE, 2>(p, max_tiles, s); break;
     case 128:
-      if (frag) launch_mx_dma<STAGE, 4>(p, max_tiles, s);
+      if (frag) launch_mx_dma<STAGE, 4, 2, 2, 4>(p, max_tiles, s);
       else launch_mx_lds<STAGE, 4>(p, max_tiles, s);
       break;
-    default: launch_mx_lds<STAGE, 8>(p, max_tiles, s); break;
+    default:
+      if (frag) launch_mx_dma<STAGE, 4, 4, 2, 4>(p, max_tiles, s);
+      else launch_mx_lds<STAGE, 8>(p, max_tiles, s);
+      break;
   }
 }
 

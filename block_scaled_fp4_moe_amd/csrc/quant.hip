@@ -66,8 +66,15 @@ __device__ __forceinline__ float e4m3_rne_sat(float v, uint32_t* code) {
 
 // ---- mxfp4_quant_1x32 ---------------------------------------------------
 
+// CHUNKED: output in the chunk-major layout, byte (c*out_rows + o)*64 +
+// (k%128)/2 for codes and (c*out_rows + o)*4 + (k%128)/32 for scales
+// (c = k/128), with output rows o = row_map[row*map_k + j] (entries outside
+// [0, out_rows) skipped) or o = row without a map; else row-major [M, K/2]
+// and [M, K/32], input row gather[row] when gather != NULL.
+template <bool CHUNKED>
 __global__ __launch_bounds__(256) void mxfp4_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, const int32_t* __restrict__ gather,
+    const int32_t* __restrict__ row_map, int map_k, int out_rows,
     const int32_t* __restrict__ row_count, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   const int chunks_per_row = K / 8;
@@ -105,8 +112,20 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(
       packed |= code << (4 * i);
     }
     if (active) {
-      *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + (int64_t)cr * 4) = packed;
-      if ((cr & 3) == 0) scales[row * (K / 32) + cr / 4] = (uint8_t)sbyte;
+      if (CHUNKED) {
+        // 16 lanes of 8 values per 128-wide chunk; one copy per mapped row
+        const int n_dst = row_map ? map_k : 1;
+        for (int j = 0; j < n_dst; ++j) {
+          const int64_t o = row_map ? (int64_t)row_map[row * map_k + j] : row;
+          if (o < 0 || o >= out_rows) continue;
+          const int64_t slab = (int64_t)(cr >> 4) * out_rows + o;
+          *reinterpret_cast<uint32_t*>(codes + slab * 64 + (cr & 15) * 4) = packed;
+          if ((cr & 3) == 0) scales[slab * 4 + ((cr & 15) >> 2)] = (uint8_t)sbyte;
+        }
+      } else {
+        *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + (int64_t)cr * 4) = packed;
+        if ((cr & 3) == 0) scales[row * (K / 32) + cr / 4] = (uint8_t)sbyte;
+      }
     }
   }
 }
@@ -217,9 +236,32 @@ extern "C" int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx,
                  "mxfp4_quant_1x32: x must be 16-byte and codes 4-byte aligned");
   FP4MOE_CHECK_DEVICE();
   const int64_t chunks = (int64_t)M * (K / 8);
-  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3(grid_for(chunks, 256)), dim3(256), 0,
-                     as_stream(stream), x, M, K, ldx, row_gather, row_count, codes, scales);
+  hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3(grid_for(chunks, 256)), dim3(256), 0,
+                     as_stream(stream), x, M, K, ldx, row_gather, nullptr, 1, M, row_count, codes,
+                     scales);
   return check_launch("mxfp4_quant_1x32");
+}
+
+extern "C" int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t ldx,
+                                        const int32_t* row_map, int map_k, int out_rows,
+                                        const int32_t* row_count, uint8_t* codes, uint8_t* scales,
+                                        void* stream) {
+  FP4MOE_REQUIRE(M >= 0 && K > 0 && K % 128 == 0,
+                 "mxfp4_quant_1x32_chunked: M=%d K=%d (K %% 128 != 0)", M, K);
+  FP4MOE_REQUIRE(ldx >= K && ldx % 8 == 0, "mxfp4_quant_1x32_chunked: ldx=%lld", (long long)ldx);
+  FP4MOE_REQUIRE(row_map ? map_k >= 1 : out_rows >= M,
+                 "mxfp4_quant_1x32_chunked: map_k=%d out_rows=%d M=%d", map_k, out_rows, M);
+  FP4MOE_REQUIRE(out_rows >= 0, "mxfp4_quant_1x32_chunked: out_rows=%d", out_rows);
+  if (M == 0 || out_rows == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(x && codes && scales, "mxfp4_quant_1x32_chunked: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 3) == 0,
+                 "mxfp4_quant_1x32_chunked: x must be 16-byte and codes 4-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  const int64_t chunks = (int64_t)M * (K / 8);
+  hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3(grid_for(chunks, 256)), dim3(256), 0,
+                     as_stream(stream), x, M, K, ldx, nullptr, row_map, map_k, out_rows,
+                     row_count, codes, scales);
+  return check_launch("mxfp4_quant_1x32_chunked");
 }
 
 extern "C" size_t nvfp4_qdq_workspace(void) { return 256; }

@@ -12,9 +12,10 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (A_BF16, A_MXFP4, LAYOUT_FRAGMENT, LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm,
-               fp4_weight_preshuffle, moe_combine, moe_permute, moe_permute_max_tiles, moe_route,
-               mxfp4_quant_1x32, nvfp4_qdq, load)
+from . import (A_BF16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
+               LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle, moe_combine,
+               moe_permute, moe_permute_max_tiles, moe_route, mxfp4_quant_1x32,
+               mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
 
 
 @dataclass
@@ -58,6 +59,12 @@ class MoELayer:
                 if cfg.wfmt != "fp8":
                     weights[name + "_scale"] = s
         self.w = weights
+        # Prefill tiles (block_m 128 / 256, MXFP4 x MXFP4, fragment weights)
+        # take their activations chunk-major and already in expert order (the
+        # stage-1 quantizer writes each token to its pairs' sorted rows), so
+        # every tile copy is contiguous.
+        self.chunked = (cfg.afmt == "mx" and cfg.wfmt == "mx" and cfg.fragment_layout
+                        and cfg.block_m in (128, 256))
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
@@ -86,7 +93,12 @@ class MoELayer:
             y=torch.empty((P, c.H), dtype=torch.bfloat16, device=dev),
             out=torch.empty((T, c.H), dtype=torch.bfloat16, device=dev),
         )
-        if c.afmt == "mx":
+        if c.afmt == "mx" and self.chunked:
+            b["xq"] = torch.empty((c.H // 128, P, 64), dtype=torch.uint8, device=dev)
+            b["xs"] = torch.empty((c.H // 128, P, 4), dtype=torch.uint8, device=dev)
+            b["hq"] = torch.empty((c.I // 128, P, 64), dtype=torch.uint8, device=dev)
+            b["hs"] = torch.empty((c.I // 128, P, 4), dtype=torch.uint8, device=dev)
+        elif c.afmt == "mx":
             b["xq"] = torch.empty((T, c.H // 2), dtype=torch.uint8, device=dev)
             b["xs"] = torch.empty((T, c.H // 32), dtype=torch.uint8, device=dev)
             b["hq"] = torch.empty((P, c.I // 2), dtype=torch.uint8, device=dev)
@@ -118,7 +130,14 @@ class MoELayer:
         wf = WFMT[c.wfmt]
         w = self.w
         tick("quant1")
-        if c.afmt == "mx":
+        gather = dict(a_row_gather=perm["sorted_pairs"], gather_div=k)
+        a_layout = A_LAYOUT_ROWMAJOR
+        if c.afmt == "mx" and self.chunked:
+            mxfp4_quant_1x32_chunked(x, row_map=perm["pair_pos"], map_k=k, codes=b["xq"],
+                                     scales=b["xs"], stream=stream)
+            a1, a1s, af = b["xq"], b["xs"], A_MXFP4
+            gather, a_layout = {}, A_LAYOUT_CHUNKED
+        elif c.afmt == "mx":
             mxfp4_quant_1x32(x, codes=b["xq"], scales=b["xs"], stream=stream)
             a1, a1s, af = b["xq"], b["xs"], A_MXFP4
         elif c.afmt == "nvfp4":
@@ -131,10 +150,14 @@ class MoELayer:
         tick("stage1")
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
-                         a_row_gather=perm["sorted_pairs"], gather_div=k, out=b["h"],
-                         w_layout=self.layout, stream=stream)
+                         out=b["h"], w_layout=self.layout, a_layout=a_layout, stream=stream,
+                         **gather)
         tick("quant2")
-        if c.afmt == "mx":
+        if c.afmt == "mx" and self.chunked:
+            mxfp4_quant_1x32_chunked(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
+                                     stream=stream)
+            a2, a2s = b["hq"], b["hs"]
+        elif c.afmt == "mx":
             mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
                              stream=stream)
             a2, a2s = b["hq"], b["hs"]
@@ -149,7 +172,7 @@ class MoELayer:
         tick("stage2")
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
                          c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
-                         out=b["y"], w_layout=self.layout, stream=stream)
+                         out=b["y"], w_layout=self.layout, a_layout=a_layout, stream=stream)
         tick("combine")
         moe_combine(b["y"], perm["pair_pos"], b["topk_w"], c.topk, c.n_shared, out=b["out"],
                     stream=stream)

@@ -63,6 +63,12 @@ enum {
   FP4MOE_A_MXFP4 = 1   /* E2M1 codes [rows, K/2] + E8M0 [rows, K/32]: gfx950 scaled MFMA    */
 };
 
+/* Layouts of MXFP4 activations (see mxfp4_quant_1x32_chunked). */
+enum {
+  FP4MOE_A_LAYOUT_ROWMAJOR = 0,  /* codes [rows, lda/2], scales [rows, lda/32]              */
+  FP4MOE_A_LAYOUT_CHUNKED = 1    /* codes [K/128][a_rows][64 B], scales [K/128][a_rows][4 B] */
+};
+
 /* Thread-local description of the last non-OK status returned on this thread. */
 const char* fp4moe_last_error(void);
 
@@ -136,6 +142,25 @@ int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx, const int32_t
                      const int32_t* row_count, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
+ * mxfp4_quant_1x32_chunked -- the same quantization as mxfp4_quant_1x32, with
+ * the output in the chunk-major layout FP4MOE_A_LAYOUT_CHUNKED that the
+ * prefill GEMM copies as whole contiguous tiles.  Output row o of a slab of
+ * out_rows rows:
+ *   codes  byte (c*out_rows + o)*64 + (k%128)/2   for element k, c = k/128
+ *   scales byte (c*out_rows + o)*4 + (k%128)/32
+ * Input row r (r < M, and r < *row_count when row_count != NULL) goes to
+ * output rows row_map[r*map_k + j], j < map_k, when row_map != NULL (stage 1
+ * passes moe_permute's pair_pos and k, so each token is read once and its
+ * codes land in expert order; entries outside [0, out_rows) are skipped),
+ * else to output row r (out_rows >= M).  Rows no input maps to are not
+ * written.  K % 128 == 0.  codes [K/128, out_rows, 64], scales
+ * [K/128, out_rows, 4].
+ */
+int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t ldx, const int32_t* row_map,
+                             int map_k, int out_rows, const int32_t* row_count, uint8_t* codes,
+                             uint8_t* scales, void* stream);
+
+/*
  * nvfp4_qdq -- NVFP4 quantize-dequantize round trip of bf16 activations.
  * [NVFP4] "Weight Dequantization and Activation QDQ".  IEEE float32 steps:
  *   s_t = tensor_scale_in ? *tensor_scale_in : amax(|x|)/2688 (1 if amax = 0)
@@ -171,6 +196,10 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * N % 32 == 0 (stage 1: N % 64 == 0); block_m in {32, 64, 128, 256} for
  * (MXFP4, MXFP4) with the output width a multiple of 64 (stage 1) or 128
  * (stage 2), block_m in {16, 32, 64} otherwise.
+ * a_layout FP4MOE_A_LAYOUT_CHUNKED (codes and scales of a_rows rows in the
+ * layout of mxfp4_quant_1x32_chunked; lda unused) is taken by (MXFP4,
+ * MXFP4) with fragment-major weights and block_m 128 or 256; other
+ * combinations return FP4MOE_ERR_INVALID_ARG.
  */
 typedef struct {
   int stage;               /* 1 or 2                                                */
@@ -198,6 +227,8 @@ typedef struct {
   int64_t ldo;             /* out row stride in elements                           */
   float* out_f32;          /* optional float32 copy before bf16 rounding, stride ldo */
   int w_layout;            /* FP4MOE_LAYOUT_* of w and w_scale                      */
+  int a_layout;            /* FP4MOE_A_LAYOUT_* of a and a_scale (MXFP4 only)       */
+  int a_rows;              /* chunked layout: rows per K chunk slab of a / a_scale  */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);

@@ -24,9 +24,9 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
-              "moe_combine", "mxfp4_to_fp8_channel"]:
+              "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked"]:
         assert n in names
     for n in names:
         assert getattr(lib, n) is not None
@@ -63,6 +63,12 @@ def test_quant_and_convert_reject_bad_K():
     st, msg = _status(lambda lib: lib.mxfp4_quant_1x32(None, 4, 48, 48, None, None, None, None,
                                                         None))
     assert st == 1 and "K" in msg
+    st, msg = _status(lambda lib: lib.mxfp4_quant_1x32_chunked(None, 4, 96, 96, None, 1, 4, None,
+                                                                None, None, None))
+    assert st == 1 and "K" in msg               # the chunked layout needs K % 128 == 0
+    st, msg = _status(lambda lib: lib.mxfp4_quant_1x32_chunked(None, 4, 128, 128, None, 1, 3, None,
+                                                                None, None, None))
+    assert st == 1 and "out_rows" in msg        # without a map every input row needs a slot
     st, msg = _status(lambda lib: lib.nvfp4_qdq(None, 4, 24, None, None, None, None, None, None,
                                                  None, 0, None))
     assert st == 1
@@ -82,7 +88,8 @@ def test_gemm_rejects_unsupported_combinations():
         args = fm.GemmArgs(a["stage"], a["wfmt"], a["afmt"], a["n_experts"], a["N"], a["K"],
                            a["max_rows"], a["max_tiles"], a["block_m"], a["gather_div"],
                            None, None, None, None, None, None, a["lda"], None, None, None, None,
-                           None, a["ldo"], None, a.get("w_layout", 0))
+                           None, a["ldo"], None, a.get("w_layout", 0), a.get("a_layout", 0),
+                           a.get("a_rows", 0))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -94,6 +101,13 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(afmt=1, block_m=16)[0] == 1
     assert run(N=96)[0] == 1
     assert run(w_layout=2)[0] == 1
+    assert run(a_layout=2)[0] == 1
+    # chunked activations: MXFP4 x MXFP4, fragment weights, block_m 128 / 256 only
+    assert run(afmt=1, block_m=128, w_layout=1, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
+    assert run(afmt=1, block_m=64, w_layout=1, a_layout=1, a_rows=8)[0] == 1
+    assert run(afmt=1, block_m=128, w_layout=0, a_layout=1, a_rows=8)[0] == 1
+    assert run(afmt=0, block_m=16, w_layout=1, a_layout=1, a_rows=8)[0] == 1
+    assert run(afmt=1, block_m=128, w_layout=1, a_layout=1, a_rows=4)[0] == 1   # < max_rows
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 
 

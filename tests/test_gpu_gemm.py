@@ -17,7 +17,7 @@ from oracle import permute as OP
 from oracle import quant as OQ
 
 from .parity import assert_bf16_close, assert_float_close
-from .test_gpu_kernels import bf16_dev, bits_of, dev, host
+from .test_gpu_kernels import bf16_dev, bits_of, chunk_major, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,7 @@ def routing(rng, T, topk, E, skew=False):
 
 
 def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
-              exact=False, layout=0):
+              exact=False, layout=0, a_layout=0):
     rng = np.random.default_rng(seed)
     Et = E + ns
     k = topk + ns
@@ -107,6 +107,18 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
     else:
         a_sorted = a_vals[:n_rows]
         gather = {}
+    if a_layout == 1:
+        # chunk-major activations, already in expert order (stage 1: gathered
+        # here, on the host), rows past the valid count poisoned
+        rows = T * k
+        if stage == 1:
+            src = np.zeros(rows, np.int64)
+            src[:n_rows] = perm_ref["sorted_pairs"][:n_rows] // k
+            qc, qs = qc[src], qs[src].copy()
+            qs[n_rows:] = 255
+        cc, cs = chunk_major(qc, qs)
+        a_kw = dict(a=dev(cc), a_scale=dev(cs), afmt=gpu_lib.A_MXFP4)
+        gather = {}
     n_out = N // 2 if stage == 1 else N
     out_f32 = torch.full((T * k, n_out), float("nan"), dtype=torch.float32, device="cuda")
     afmt_code = a_kw.pop("afmt")
@@ -118,7 +130,7 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
             wkw["w_scale"] = sc
     out = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.WFMT[wfmt], afmt_code,
                                    perm=perm, block_m=bm, out_f32=out_f32, w_layout=layout,
-                                   **wkw, **a_kw, **gather)
+                                   a_layout=a_layout, **wkw, **a_kw, **gather)
     ref_unrounded = OG.grouped_stage(stage, a_sorted, perm_ref["expert_offsets"],
                                      lambda e: oracle_weight(wd, wfmt, e), rounding=False)
     g_bits = bits_of(out)[:n_rows]
@@ -162,6 +174,10 @@ MX_CASES = [
     (2, "mx", 200, 3, 6, 1, 512, 256, 64, 24, True),
     (1, "mx", 400, 4, 8, 1, 512, 256, 128, 25, True),
     (2, "mx", 400, 4, 8, 1, 512, 256, 256, 26, True),
+    (1, "mx", 400, 4, 8, 1, 512, 256, 256, 33, True),
+    (1, "mx", 300, 8, 8, 1, 1024, 512, 256, 34, False),
+    (2, "mx", 300, 8, 8, 1, 1024, 512, 256, 35, False),
+    (1, "mx", 300, 8, 8, 1, 1024, 512, 128, 36, False),
     (1, "mx", 5, 2, 4, 1, 7168, 2048, 32, 27, False),
     (2, "mx", 5, 2, 4, 1, 7168, 2048, 32, 28, False),
     (1, "fp8", 150, 3, 6, 1, 512, 256, 64, 29, True),
@@ -175,6 +191,14 @@ MX_CASES = [
 def test_mx_gemm_parity(gpu_lib, case, layout):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
     run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew, layout=layout)
+
+
+@pytest.mark.parametrize("case", [c for c in MX_CASES if c[1] == "mx" and c[8] >= 128])
+def test_mx_gemm_chunked_activations(gpu_lib, case):
+    """Prefill tiles reading chunk-major, pre-gathered MXFP4 activations."""
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=gpu_lib.A_LAYOUT_CHUNKED)
 
 
 @pytest.mark.parametrize("afmt,bm,layout", [("bf16", 16, 0), ("bf16", 64, 1), ("mx", 64, 0),

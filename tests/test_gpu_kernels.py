@@ -170,6 +170,52 @@ def test_mxfp4_quant_gather_and_row_count(gpu_lib):
     assert np.all(host(codes)[51:] == 0xAB) and np.all(host(scales)[51:] == 0xCD)
 
 
+def chunk_major(codes, scales):
+    """Row-major MXFP4 codes [M, K/2] / scales [M, K/32] in the chunk-major
+    layout: codes [K/128, M, 64], scales [K/128, M, 4] (an index permutation)."""
+    M, kb = codes.shape
+    return (np.ascontiguousarray(codes.reshape(M, kb // 64, 64).transpose(1, 0, 2)),
+            np.ascontiguousarray(scales.reshape(M, kb // 64, 4).transpose(1, 0, 2)))
+
+
+@pytest.mark.parametrize("M,K", [(8, 128), (37, 512), (64, 7168)])
+def test_mxfp4_quant_chunked_parity(gpu_lib, M, K):
+    xb = _quant_inputs(M * 3 + K, M, K)
+    codes, scales = gpu_lib.mxfp4_quant_1x32_chunked(bf16_dev(xb))
+    rc, rs = chunk_major(*OQ.mxfp4_quant_1x32(xb))
+    assert_equal(host(scales), rs, "chunked scales")
+    assert_equal(host(codes), rc, "chunked codes")
+
+
+def test_mxfp4_quant_chunked_scatter_and_row_count(gpu_lib):
+    xb = _quant_inputs(9, 30, 256)
+    k = 3
+    g = np.random.default_rng(8)
+    pos = g.permutation(30 * k).astype(np.int32)          # pair (t, j) -> sorted row
+    pos[g.choice(30 * k, 7, replace=False)] = -1           # dropped pairs
+    pos[5] = 10**6                                         # out of range: skipped
+    codes = torch.full((2, 90, 64), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((2, 90, 4), 0xCD, dtype=torch.uint8, device="cuda")
+    gpu_lib.mxfp4_quant_1x32_chunked(bf16_dev(xb), row_map=dev(pos), map_k=k, codes=codes,
+                                     scales=scales)
+    rc, rs = chunk_major(*OQ.mxfp4_quant_1x32(xb))
+    hc, hs = host(codes), host(scales)
+    written = np.zeros(90, bool)
+    for p_, o in enumerate(pos):
+        if 0 <= o < 90:
+            written[o] = True
+            assert_equal(hc[:, o], rc[:, p_ // k], f"row {o}")
+            assert_equal(hs[:, o], rs[:, p_ // k], f"scale row {o}")
+    assert np.all(hc[:, ~written] == 0xAB) and np.all(hs[:, ~written] == 0xCD)
+    # row_count limits the input rows without a map
+    codes2, scales2 = gpu_lib.mxfp4_quant_1x32_chunked(
+        bf16_dev(xb), row_count=dev(np.array([11], np.int32)),
+        codes=torch.full((2, 30, 64), 0xAB, dtype=torch.uint8, device="cuda"),
+        scales=torch.full((2, 30, 4), 0xCD, dtype=torch.uint8, device="cuda"))
+    assert_equal(host(codes2)[:, :11], rc[:, :11], "row_count codes")
+    assert np.all(host(codes2)[:, 11:] == 0xAB) and np.all(host(scales2)[:, 11:] == 0xCD)
+
+
 # ------------------------------------------------------------------ NVFP4 QDQ
 
 @pytest.mark.parametrize("M,K,static", [(16, 256, False), (64, 7168, False), (33, 2048, True)])

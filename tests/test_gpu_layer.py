@@ -131,8 +131,9 @@ def test_layer_decode_full_width(gpu_lib, T):
     run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
 
 
-def test_layer_prefill_path_full_width(gpu_lib):
-    run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", 64)
+@pytest.mark.parametrize("block_m", [64, 256])
+def test_layer_prefill_path_full_width(gpu_lib, block_m):
+    run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", block_m)
 
 
 def test_layer_nvfp4_full_width(gpu_lib):
