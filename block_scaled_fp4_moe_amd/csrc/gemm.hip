@@ -119,6 +119,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   const int mt = a->max_tiles;
   const int st = a->stage;
   if (mx) launch_mx_gemm(p, st, mt, s);
+  else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");
 }

@@ -125,6 +125,44 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
 
 __device__ __forceinline__ v8bf as_bf8(uint4 v) { return __builtin_bit_cast(v8bf, v); }
 
+// ---- LDS-DMA helpers (global_load_lds_*), shared by the tiled GEMMs ------
+
+__device__ __forceinline__ uint32_t lds_offset(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+
+// Every lane copies 16 (4) bytes from its own global address to LDS at the
+// wave-uniform byte offset `lds` + 16 (4) * lane.
+// The LDS offset goes to M0 through a register constraint, so the compiler
+// owns M0 (and its hazards) around the copy.
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :: "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off"
+               :: "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maximum) as a builtin,
+// so that the compiler's own wait insertion knows the LDS reads are complete.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Wait until at most `newer` chunks (D DMA instructions each) issued after the
+// current one are still in flight.
+template <int D, int SM2>
+__device__ __forceinline__ void wait_chunks(int newer) {
+  if (SM2 >= 4 && newer >= 4) wait_vmcnt<(SM2 >= 4 ? 4 : 0) * D>();
+  else if (SM2 >= 3 && newer == 3) wait_vmcnt<(SM2 >= 3 ? 3 : 0) * D>();
+  else if (SM2 >= 2 && newer == 2) wait_vmcnt<(SM2 >= 2 ? 2 : 0) * D>();
+  else if (newer == 1) wait_vmcnt<D>();
+  else wait_vmcnt<0>();
+}
+
 // Workgroups that fill the device: 8 per compute unit (queried once).
 int grid_cap();
 
@@ -132,5 +170,9 @@ int grid_cap();
 void launch_dq_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
                     hipStream_t s);
 void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+// Tiled dq variant (64-row tiles, fragment weights): whether it takes `p`.
+bool dqt_supported(const GemmParams& p, int stage);
+void launch_dqt_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
+                     hipStream_t s);
 
 }  // namespace fp4moe

@@ -366,42 +366,6 @@ __global__ __launch_bounds__(256, 1) void mx_lds_gemm_kernel(GemmParams p) {
 // barrier into the stage computed in the previous step, so S-1 chunks are in
 // flight while one is computed.  The loads are issued from inline assembly so
 // that the compiler does not drain the whole ring at every barrier.
-__device__ __forceinline__ uint32_t lds_offset(const void* ptr) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
-}
-
-// Every lane copies 16 (4) bytes from its own global address to LDS at the
-// wave-uniform byte offset `lds` + 16 (4) * lane.
-// The LDS offset goes to M0 through a register constraint, so the compiler
-// owns M0 (and its hazards) around the copy.
-__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off"
-               :: "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
-  asm volatile("global_load_lds_dword %0, off"
-               :: "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// s_waitcnt lgkmcnt(0) (vmcnt and expcnt left at their maximum) as a builtin,
-// so that the compiler's own wait insertion knows the LDS reads are complete.
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// Wait until at most `newer` chunks (D DMA instructions each) issued after the
-// current one are still in flight.
-template <int D, int SM2>
-__device__ __forceinline__ void wait_chunks(int newer) {
-  if (SM2 >= 4 && newer >= 4) wait_vmcnt<(SM2 >= 4 ? 4 : 0) * D>();
-  else if (SM2 >= 3 && newer == 3) wait_vmcnt<(SM2 >= 3 ? 3 : 0) * D>();
-  else if (SM2 >= 2 && newer == 2) wait_vmcnt<(SM2 >= 2 ? 2 : 0) * D>();
-  else if (newer == 1) wait_vmcnt<D>();
-  else wait_vmcnt<0>();
-}
-
 // WAVES_M x WAVES_N waves (4 in all); each wave owns WM M blocks x 8 weight
 // groups of 16 rows (a 16*WM x 128 sub-tile, 32 MFMA tiles).  The
 // workgroup tile is BM = 16*WM*WAVES_M rows by 128*WAVES_N weight rows.
@@ -635,6 +599,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
     } else {
       for (int c = 0; c < nkc; ++c) {
         wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));
+        wait_lgkm0();   // this wave's reads of chunk c-1 are complete: its stage is refilled next
         wg_barrier();
         if (c + S - 1 < nkc) issue(c + S - 1, c + S - 1);
         read_ops(c);

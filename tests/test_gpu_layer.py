@@ -136,9 +136,11 @@ def test_layer_prefill_path_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", block_m)
 
 
-def test_layer_nvfp4_full_width(gpu_lib):
-    run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", 16)
+@pytest.mark.parametrize("block_m", [16, 64])
+def test_layer_nvfp4_full_width(gpu_lib, block_m):
+    run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", block_m)
 
 
-def test_layer_fp8_full_width(gpu_lib):
-    run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", 32)
+@pytest.mark.parametrize("block_m", [32, 64])
+def test_layer_fp8_full_width(gpu_lib, block_m):
+    run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", block_m)
