@@ -47,11 +47,14 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                    "fp4_grouped_gemm: block_m=%d not in {16,32,64} for this format pair",
                    a->block_m);
   } else {
-    FP4MOE_REQUIRE(a->block_m == 32 || a->block_m == 64 || a->block_m == 128 || a->block_m == 256,
-                   "fp4_grouped_gemm: block_m=%d not in {32,64,128,256} for MXFP4 x MXFP4",
+    FP4MOE_REQUIRE(a->block_m == 32 || a->block_m == 64 || a->block_m == 128 ||
+                       a->block_m == 192 || a->block_m == 256,
+                   "fp4_grouped_gemm: block_m=%d not in {32,64,128,192,256} for MXFP4 x MXFP4",
                    a->block_m);
+    FP4MOE_REQUIRE(a->block_m != 192 || a->w_layout == FP4MOE_LAYOUT_FRAGMENT,
+                   "fp4_grouped_gemm: block_m 192 needs fragment-major weights");
     const bool big = a->block_m >= 128;
-    const int out_per_wg = (a->stage == 1 ? 64 : 128) * (big ? 2 : 1);
+    const int out_per_wg = (a->stage == 1 ? 64 : 128) * (a->block_m == 192 ? 4 : big ? 2 : 1);
     const int n_out = a->stage == 1 ? a->N / 2 : a->N;
     FP4MOE_REQUIRE(n_out % out_per_wg == 0,
                    "fp4_grouped_gemm: output width %d not a multiple of %d", n_out, out_per_wg);
@@ -68,12 +71,18 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: a_layout=%d", a->a_layout);
   const bool a_chunked = a->a_layout == FP4MOE_A_LAYOUT_CHUNKED;
   FP4MOE_REQUIRE(!a_chunked || (mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
-                                (a->block_m == 128 || a->block_m == 256)),
+                                (a->block_m == 128 || a->block_m == 192 || a->block_m == 256)),
                  "fp4_grouped_gemm: chunked activations need MXFP4 x MXFP4, fragment weights "
-                 "and block_m 128 or 256");
+                 "and block_m 128, 192 or 256");
   FP4MOE_REQUIRE(!a_chunked || (a->a_rows >= 1 && a->a_rows <= (1 << 26) &&
                                 (a->a_row_gather || a->a_rows >= a->max_rows)),
                  "fp4_grouped_gemm: a_rows=%d (max_rows=%d)", a->a_rows, a->max_rows);
+  // the LDS-DMA tiles (MXFP4 x MXFP4, fragment weights, block_m >= 128) address
+  // row-major A rows with 32-bit byte offsets
+  FP4MOE_REQUIRE(!(mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT && a->block_m >= 128 && !a_chunked) ||
+                     (int64_t)a->max_rows * (a->lda / 2) <= (int64_t)0xffffffff,
+                 "fp4_grouped_gemm: row-major A of %d rows x lda %lld exceeds 4 GiB for block_m %d",
+                 a->max_rows, (long long)a->lda, a->block_m);
   const int n_out = a->stage == 1 ? a->N / 2 : a->N;
   FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
   FP4MOE_REQUIRE(a_chunked || (a->lda >= a->K && a->lda % 32 == 0), "fp4_grouped_gemm: lda=%lld",

@@ -642,6 +642,258 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
   }
 }
 
+// ---------------------------------------------------------------------------
+// mx family, wide tiles (block_m 192): 192 rows x 512 weight rows.
+//
+// At prefill sizes every weight byte comes from HBM once, while the
+// activation rows of an expert are copied again for every column block of
+// its weights.  A 192 x 512 tile needs half the activation copies of a
+// 256 x 256 tile per weight byte, and 192 rows cover a uniformly routed
+// expert (about T*k/E rows) with less padding.  The accumulators of the tile
+// fill 3/4 of the register file: 8 waves (2 per SIMD) in a 2 (M) x 4 (N)
+// grid, each wave 96 x 128 as 3 x 4 tiles of the 32x32x64 scaled MFMA, 192
+// accumulator registers per lane.  That leaves room for the operands of one
+// 64-wide K step only, so the ping-pong of the two waves of a SIMD runs at
+// K-step granularity: per step a read phase (operands of one K step from
+// LDS) and a multiply phase (12 MFMAs), one barrier each.
+// Ring: 3 stages of one 128-wide K chunk (activation codes 12 KiB + scales
+// 768 B, weight fragments 32 KiB + scales 2 KiB).  Every wave issues 7 DMA
+// instructions per chunk: waves 0-3 two activation fragments, waves 4-7 one
+// fragment and one 64-row scale copy (wave 7 repeats wave 6's scale copy:
+// the same bytes to the same LDS addresses), then 4 weight fragments and
+// their scales.
+// LDS-DMA with a wave-uniform 64-bit base in scalar registers and a 32-bit
+// per-lane byte offset (the saddr form): one VGPR per address instead of two.
+__device__ __forceinline__ void dma_b128_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+__device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+template <int STAGE>
+__global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) {
+  constexpr int S = 3, NW = 8, BM = 192;
+  constexpr int WM = 6, MT = 3;                     // 16-row blocks / 32-row tiles per wave
+  constexpr int WN = 8, NT = 4;                     // weight groups / 32-row tiles per wave
+  constexpr int NG_WG = 32, GPW = 4;                // weight groups per workgroup / per copying wave
+  constexpr int OUT_PER_WAVE = (STAGE == 1) ? (WN / 2) * 16 : WN * 16;
+  constexpr int OUT_PER_WG = 4 * OUT_PER_WAVE;
+  constexpr int OFF_AS = BM * 64;                   // A codes: [12 blocks][64 lanes][16 B]
+  constexpr int OFF_B = OFF_AS + BM * 4;            // A scales: [row][4 blocks]
+  constexpr int OFF_BS = OFF_B + NG_WG * 1024;      // B codes: [32 groups][64 lanes][16 B]
+  constexpr int STAGE_BYTES = OFF_BS + NW * 256;    // B scales: [8 waves][4 groups][64 B]
+  constexpr int D = 7;                              // DMA instructions per wave per chunk
+  static_assert(S * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert(OFF_B % 16 == 0 && OFF_BS % 16 == 0 && STAGE_BYTES % 16 == 0, "alignment");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;                        // ping-pong group; also the M half
+  const int wm = grp, wn = wave & 3;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
+  const int n_nb = n_out / OUT_PER_WG;
+  const int nkc = p.K / 128;
+  const int G = p.N / 16;
+  const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
+  const uint8_t* A = static_cast<const uint8_t*>(p.a);
+  const bool chunked = p.a_layout == FP4MOE_A_LAYOUT_CHUNKED;
+  const int64_t a_row_bytes = chunked ? 64 : p.lda / 2, a_srow = chunked ? 4 : p.lda / 32;
+  const int64_t a_cstride = chunked ? (int64_t)p.a_rows * 64 : 64;
+  const int64_t as_cstride = chunked ? (int64_t)p.a_rows * 4 : 4;
+  const uint32_t smem_base = lds_offset(smem);
+
+  constexpr int NX = 8;
+  const int xcd = blockIdx.x % NX, slot = blockIdx.x / NX;
+  const int slots = ((int)gridDim.x - xcd + NX - 1) / NX;
+  const int64_t per = (n_work + NX - 1) / NX;
+  const int64_t w_begin = (int64_t)xcd * per;
+  const int64_t w_end = min(n_work, w_begin + per);
+
+  // LDS read bases (see mx_dma_gemm_kernel): lane l of K step h reads
+  // fragment (l % 32) / 16 at lane' l % 16 + 16 * (2h + l / 32)
+  const int m16 = (lane & 31) >> 4, kb = lane >> 5;
+  const int frag_lane = m16 * 1024 + (lane & 15) * 16 + kb * 256;
+  const int a_lds = wm * WM * 1024 + frag_lane;
+  const int as_lds = OFF_AS + wm * WM * 64 + (lane & 31) * 4 + kb;
+  const int b_lds = OFF_B + frag_lane;
+  const int bs_lds = OFF_BS + m16 * 64 + (lane & 15) + 16 * kb;
+
+  for (int64_t wi = w_begin + slot; wi < w_end; wi += slots) {
+    const int any_tile = (int)(wi / n_nb);
+    const int e = p.tiles[2 * any_tile];
+    const int t0 = any_tile - p.tiles[2 * any_tile + 1];
+    const int m_tiles = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+    const int local = (int)(wi - (int64_t)t0 * n_nb);
+    const int nb = local / m_tiles, mt = local - nb * m_tiles;
+    const int tile_row0 = p.offsets[e] + mt * BM;
+    const int row_end = min(p.offsets[e + 1], tile_row0 + BM);
+
+    auto src_row = [&](int r) -> int64_t {
+      if (r >= row_end) return 0;
+      return p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
+    };
+    // activation copies of this wave: fragments f0 (and f0+1 for waves 0-3),
+    // waves 4-7 also one 64-row scale block
+    const int f0 = grp == 0 ? 2 * wave : wave + 4;
+    const uint32_t a_off0 = (uint32_t)(src_row(tile_row0 + f0 * 16 + r16) * a_row_bytes) + g * 16;
+    const uint32_t a_off1 = (uint32_t)(src_row(tile_row0 + (f0 + 1) * 16 + r16) * a_row_bytes) + g * 16;
+    const int sblk = grp == 0 ? 0 : min(wave - 4, 2);
+    const uint32_t as_off = (uint32_t)(src_row(tile_row0 + sblk * 64 + lane) * a_srow);
+    // weight groups [4w, 4w+4) of the workgroup: stage 1 gate groups then up groups
+    int grp0;
+    {
+      const int j0 = wave * GPW;
+      if (STAGE == 1)
+        grp0 = (j0 < NG_WG / 2) ? nb * (NG_WG / 2) + j0 : G / 2 + nb * (NG_WG / 2) + (j0 - NG_WG / 2);
+      else
+        grp0 = nb * NG_WG + j0;
+    }
+    const uint8_t* b_base = p.w + ((int64_t)e * G + grp0) * nkc * 1024;
+    const uint8_t* bs_base = p.w_scale + ((int64_t)e * nkc * G + grp0) * 64;
+
+    auto issue = [&](int c) {
+      const uint32_t st = smem_base + (uint32_t)((c % S) * STAGE_BYTES);
+      const uint8_t* a_c = A + (int64_t)c * a_cstride;
+      if (grp == 0) {
+        dma_b128_s(a_c, a_off0, st + f0 * 1024);
+        dma_b128_s(a_c, a_off1, st + (f0 + 1) * 1024);
+      } else {
+        dma_b128_s(a_c, a_off0, st + f0 * 1024);
+        dma_b32_s(p.a_scale + (int64_t)c * as_cstride, as_off, st + OFF_AS + sblk * 256);
+      }
+#pragma unroll
+      for (int q = 0; q < GPW; ++q)
+        dma_b128_s(b_base + ((int64_t)q * nkc + c) * 1024, lane * 16, st + OFF_B + (wave * GPW + q) * 1024);
+      dma_b32_s(bs_base + (int64_t)c * G * 64, lane * 4, st + OFF_BS + wave * 256);
+    };
+
+    v16f acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
+
+    v4u bo[NT], ao[MT];
+    int bso[NT], aso[MT];
+    auto read_ops = [&](int c, int h) {
+      const uint8_t* st = smem + (c % S) * STAGE_BYTES;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int ju = (STAGE == 1)
+                           ? ((nt < NT / 2) ? wn * (WN / 2) + nt * 2 : NG_WG / 2 + wn * (WN / 2) + (nt - NT / 2) * 2)
+                           : wn * WN + nt * 2;
+        bo[nt] = *reinterpret_cast<const v4u*>(st + b_lds + ju * 1024 + h * 512);
+        bso[nt] = st[bs_lds + (ju / GPW) * 256 + (ju % GPW) * 64 + h * 32];
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        ao[i] = *reinterpret_cast<const v4u*>(st + a_lds + i * 2048 + h * 512);
+        aso[i] = st[as_lds + i * 128 + 2 * h];
+      }
+    };
+    auto mma = [&]() {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const v8i af = v8i{(int)ao[i][0], (int)ao[i][1], (int)ao[i][2], (int)ao[i][3], 0, 0, 0, 0};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3], 0, 0, 0, 0};
+          acc[i][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][nt], 4, 4, 0,
+                                                                      aso[i], 0, bso[nt]);
+        }
+      }
+    };
+
+    // Steps s = 2c + h.  Waves 0-3 pass barrier 2s before reading step s and
+    // barrier 2s+1 before multiplying it; waves 4-7 run one barrier behind
+    // (one extra barrier at the start, waves 0-3 one at the end).  Chunk c
+    // has landed (every wave's copies) before barrier 4c: waves 0-3 wait
+    // right before it, waves 4-7 before their second barrier of step 2c-1.
+    // The refill of chunk c+2 goes into chunk c-1's stage, issued after
+    // barrier 4c (4c+1 for waves 4-7); chunk c-1 was last read before 4c.
+    for (int c = 0; c < S - 1 && c < nkc; ++c) issue(c);
+    if (grp == 1) {
+      wait_chunks<D, S - 2>(min(S - 2, nkc - 1));
+      wg_barrier();
+    }
+    for (int c = 0; c < nkc; ++c) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 0) wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));
+        wait_lgkm0();
+        asm volatile("s_barrier"
+                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                       "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]),
+                       "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[2][2]), "+v"(acc[2][3])
+                     :
+                     : "memory");
+        if (h == 0 && c + S - 1 < nkc) issue(c + S - 1);
+        read_ops(c, h);
+        if (h == 1 && grp == 1 && c + 1 < nkc) wait_chunks<D, S - 2>(min(S - 2, nkc - 2 - c));
+        wait_lgkm0();
+        asm volatile("s_barrier"
+                     : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo[2]), "+v"(bo[3]),
+                       "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]),
+                       "+v"(bso[0]), "+v"(bso[1]), "+v"(bso[2]), "+v"(bso[3]),
+                       "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[2])
+                     :
+                     : "memory");
+        mma();
+      }
+    }
+    if (grp == 0) wg_barrier();
+    wg_barrier();   // every wave is done with the ring before the next item refills it
+
+    // epilogue: lane l holds column l % 32 of each 32x32 tile and rows
+    // (i / 4) * 8 + (l / 32) * 4 + i % 4 in accumulator element i
+    const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane & 31);
+    const int wrow0 = tile_row0 + wm * WM * 16 + kb * 4;
+#pragma unroll
+    for (int i3 = 0; i3 < MT; ++i3) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = wrow0 + i3 * 32 + (i >> 2) * 8 + (i & 3);
+        if (r >= row_end) continue;
+        if (STAGE == 1) {
+#pragma unroll
+          for (int j = 0; j < NT / 2; ++j) {
+            const float hv = silu_mul(acc[i3][j][i], acc[i3][j + NT / 2][i]);
+            const int64_t o = (int64_t)r * p.ldo + col0 + j * 32;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(hv);
+            if (p.out_f32) p.out_f32[o] = hv;
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            const float y = acc[i3][nt][i];
+            const int64_t o = (int64_t)r * p.ldo + col0 + nt * 32;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(y);
+            if (p.out_f32) p.out_f32[o] = y;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+template <int STAGE>
+static void launch_mx_wide(const GemmParams& p, int max_tiles, hipStream_t s) {
+  const int out_per_wg = (STAGE == 1) ? 256 : 512;
+  const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
+  const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
+  const int cap = grid_cap() / 8;        // one workgroup (eight waves) per CU
+  const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
+  hipLaunchKernelGGL((mx_dma_wide_gemm_kernel<STAGE>), dim3(grid), dim3(512), 0, s, p);
+}
+
 template <int STAGE, int WM>
 static void launch_mx_wm(const GemmParams& p, int max_tiles, hipStream_t s) {
   constexpr int WN = 4;
@@ -683,6 +935,7 @@ static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
       if (frag) launch_mx_dma<STAGE, 4, 2, 2, 4>(p, max_tiles, s);
       else launch_mx_lds<STAGE, 4>(p, max_tiles, s);
       break;
+    case 192: launch_mx_wide<STAGE>(p, max_tiles, s); break;   // fragment weights only
     default:
       if (frag) launch_mx_dma<STAGE, 4, 4, 2, 4>(p, max_tiles, s);
       else launch_mx_lds<STAGE, 8>(p, max_tiles, s);

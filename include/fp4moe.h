@@ -193,12 +193,15 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * Supported (wfmt, afmt): (MXFP4, BF16), (NVFP4, BF16), (FP8, BF16),
  * (FP8, MXFP4) -- operands decoded exactly to bf16 in registers, bf16 MFMA --
  * and (MXFP4, MXFP4) -- gfx950 scaled MFMA FP4 x FP4.  K % 128 == 0,
- * N % 32 == 0 (stage 1: N % 64 == 0); block_m in {32, 64, 128, 256} for
- * (MXFP4, MXFP4) with the output width a multiple of 64 (stage 1) or 128
- * (stage 2), block_m in {16, 32, 64} otherwise.
+ * N % 32 == 0 (stage 1: N % 64 == 0); block_m in {32, 64, 128, 192, 256}
+ * for (MXFP4, MXFP4) with the output width a multiple of 64 (stage 1) or 128
+ * (stage 2) -- block_m 128 / 256: 128 / 256, block_m 192: 256 / 512, and
+ * block_m 192 only with fragment-major weights -- block_m in {16, 32, 64}
+ * otherwise.  (MXFP4, MXFP4) with fragment-major weights, block_m >= 128 and
+ * row-major A needs max_rows * lda / 2 < 2^32 and gathered rows < max_rows.
  * a_layout FP4MOE_A_LAYOUT_CHUNKED (codes and scales of a_rows rows in the
  * layout of mxfp4_quant_1x32_chunked; lda unused) is taken by (MXFP4,
- * MXFP4) with fragment-major weights and block_m 128 or 256; other
+ * MXFP4) with fragment-major weights and block_m 128, 192 or 256; other
  * combinations return FP4MOE_ERR_INVALID_ARG.
  */
 typedef struct {

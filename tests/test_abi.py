@@ -102,12 +102,22 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(N=96)[0] == 1
     assert run(w_layout=2)[0] == 1
     assert run(a_layout=2)[0] == 1
-    # chunked activations: MXFP4 x MXFP4, fragment weights, block_m 128 / 256 only
+    # chunked activations: MXFP4 x MXFP4, fragment weights, block_m 128 / 192 / 256 only
     assert run(afmt=1, block_m=128, w_layout=1, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
     assert run(afmt=1, block_m=64, w_layout=1, a_layout=1, a_rows=8)[0] == 1
     assert run(afmt=1, block_m=128, w_layout=0, a_layout=1, a_rows=8)[0] == 1
     assert run(afmt=0, block_m=16, w_layout=1, a_layout=1, a_rows=8)[0] == 1
     assert run(afmt=1, block_m=128, w_layout=1, a_layout=1, a_rows=4)[0] == 1   # < max_rows
+    # block_m 192: MXFP4 x MXFP4 with fragment weights, output width a multiple
+    # of 256 (stage 1) / 512 (stage 2)
+    wide = dict(afmt=1, block_m=192, w_layout=1, N=512, ldo=512)
+    assert run(**wide, max_tiles=0)[0] == 0
+    assert run(**{**wide, "w_layout": 0})[0] == 1
+    assert run(**{**wide, "N": 256})[0] == 1
+    assert run(**{**wide, "N": 256}, stage=2, max_tiles=0)[0] == 1
+    assert run(**wide, stage=2, max_tiles=0)[0] == 0
+    assert run(**wide, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
+    assert run(**{**wide, "block_m": 160})[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 
 

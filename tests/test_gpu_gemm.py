@@ -185,6 +185,17 @@ MX_CASES = [
     (1, "fp8", 3, 2, 4, 1, 7168, 2048, 16, 32, False),
 ]
 
+# block_m 192 (192 x 512 tiles, fragment-major weights only): experts of one
+# and two M tiles, K of 1, 2 and several 128-wide chunks
+WIDE_CASES = [
+    (1, "mx", 400, 4, 8, 1, 512, 256, 192, 37, True),
+    (2, "mx", 400, 4, 8, 1, 512, 256, 192, 38, True),
+    (1, "mx", 300, 8, 8, 1, 1024, 512, 192, 39, False),
+    (2, "mx", 300, 8, 8, 1, 1024, 512, 192, 40, False),
+    (1, "mx", 100, 2, 4, 0, 128, 256, 192, 41, False),
+    (2, "mx", 100, 2, 4, 0, 512, 128, 192, 42, False),
+]
+
 
 @pytest.mark.parametrize("layout", [0, 1])
 @pytest.mark.parametrize("case", MX_CASES)
@@ -193,7 +204,15 @@ def test_mx_gemm_parity(gpu_lib, case, layout):
     run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew, layout=layout)
 
 
-@pytest.mark.parametrize("case", [c for c in MX_CASES if c[1] == "mx" and c[8] >= 128])
+@pytest.mark.parametrize("case", WIDE_CASES)
+def test_mx_gemm_wide_tiles(gpu_lib, case):
+    """192 x 512 tiles with row-major activations."""
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT)
+
+
+@pytest.mark.parametrize("case", [c for c in MX_CASES + WIDE_CASES if c[1] == "mx" and c[8] >= 128])
 def test_mx_gemm_chunked_activations(gpu_lib, case):
     """Prefill tiles reading chunk-major, pre-gathered MXFP4 activations."""
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case

@@ -131,7 +131,7 @@ def test_layer_decode_full_width(gpu_lib, T):
     run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
 
 
-@pytest.mark.parametrize("block_m", [64, 256])
+@pytest.mark.parametrize("block_m", [64, 192, 256])
 def test_layer_prefill_path_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", block_m)
 
