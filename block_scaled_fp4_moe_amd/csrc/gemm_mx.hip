@@ -686,6 +686,10 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   constexpr int OFF_BS = OFF_B + NG_WG * 1024;      // B codes: [32 groups][64 lanes][16 B]
   constexpr int STAGE_BYTES = OFF_BS + NW * 256;    // B scales: [8 waves][4 groups][64 B]
   constexpr int D = 7;                              // DMA instructions per wave per chunk
+  constexpr int EP_TILES = (STAGE == 1) ? NT / 2 : NT;   // 32-column output tiles per wave
+  constexpr int EP_COLS = 32 * EP_TILES;            // output columns per wave
+  constexpr int EP_PITCH = EP_COLS * 2 + 64;        // epilogue LDS row: bf16 + bank skew
+  static_assert(8 * 16 * EP_PITCH <= STAGE_BYTES, "epilogue buffers fit in one ring stage");
   static_assert(S * STAGE_BYTES <= 160 * 1024, "LDS");
   static_assert(OFF_B % 16 == 0 && OFF_BS % 16 == 0 && STAGE_BYTES % 16 == 0, "alignment");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE_BYTES];
@@ -853,33 +857,74 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
 
     // epilogue: lane l holds column l % 32 of each 32x32 tile and rows
     // (i / 4) * 8 + (l / 32) * 4 + i % 4 in accumulator element i
-    const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane & 31);
-    const int wrow0 = tile_row0 + wm * WM * 16 + kb * 4;
+    const int wrow0 = tile_row0 + wm * WM * 16;
+    if (p.out_f32) {
+      // fp32 copy requested: element-wise stores of both outputs
+      const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane & 31);
 #pragma unroll
-    for (int i3 = 0; i3 < MT; ++i3) {
+      for (int i3 = 0; i3 < MT; ++i3) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = wrow0 + i3 * 32 + (i >> 2) * 8 + (i & 3);
-        if (r >= row_end) continue;
-        if (STAGE == 1) {
+        for (int i = 0; i < 16; ++i) {
+          const int r = wrow0 + kb * 4 + i3 * 32 + (i >> 2) * 8 + (i & 3);
+          if (r >= row_end) continue;
 #pragma unroll
-          for (int j = 0; j < NT / 2; ++j) {
-            const float hv = silu_mul(acc[i3][j][i], acc[i3][j + NT / 2][i]);
+          for (int j = 0; j < EP_TILES; ++j) {
+            const float y = (STAGE == 1) ? silu_mul(acc[i3][j][i], acc[i3][j + NT / 2][i]) : acc[i3][j][i];
             const int64_t o = (int64_t)r * p.ldo + col0 + j * 32;
-            p.out[o] = (uint16_t)f32_to_bf16_rne(hv);
-            if (p.out_f32) p.out_f32[o] = hv;
-          }
-        } else {
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            const float y = acc[i3][nt][i];
-            const int64_t o = (int64_t)r * p.ldo + col0 + nt * 32;
             p.out[o] = (uint16_t)f32_to_bf16_rne(y);
-            if (p.out_f32) p.out_f32[o] = y;
+            p.out_f32[o] = y;
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      // bf16 only: 16 rows at a time through this wave's slice of ring stage
+      // 2 (the next item's prologue fills stages 0 and 1 only, and stage 2
+      // after a barrier every wave passes once its epilogue is done), then
+      // 16-byte row stores.  Lanes 2m and 2m+1 (columns 2m, 2m+1) swap one
+      // value per row pair so that each writes one dword (two columns) of
+      // one row: the even lane row i, the odd lane row i+1.
+      uint8_t* ep = smem + 2 * STAGE_BYTES + wave * 16 * EP_PITCH;
+      const bool odd = lane & 1;
+      const int cpair = ((lane & 31) & ~1) * 2;     // byte offset of the column pair
+      constexpr int LPR = EP_COLS * 2 / 16;         // lanes per 16-byte row piece set
+      constexpr int RPI = 64 / LPR;                 // rows per 64-lane store
+      const int64_t out_col = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane % LPR) * 8;
+#pragma unroll
+      for (int i3 = 0; i3 < MT; ++i3) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int j = 0; j < EP_TILES; ++j) {
+#pragma unroll
+            for (int i = 8 * hh; i < 8 * hh + 8; i += 2) {
+              float v0, v1;
+              if (STAGE == 1) {
+                v0 = silu_mul(acc[i3][j][i], acc[i3][j + NT / 2][i]);
+                v1 = silu_mul(acc[i3][j][i + 1], acc[i3][j + NT / 2][i + 1]);
+              } else {
+                v0 = acc[i3][j][i];
+                v1 = acc[i3][j][i + 1];
+              }
+              const float send = odd ? v0 : v1;
+              const float recv = __int_as_float(
+                  __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+              const float lo = odd ? recv : v0, hi = odd ? v1 : recv;
+              const uint32_t packed = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+              const int row = (i >> 2) * 8 + kb * 4 + (i & 3) + (odd ? 1 : 0) - 16 * hh;
+              *reinterpret_cast<uint32_t*>(ep + row * EP_PITCH + j * 64 + cpair) = packed;
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 16 / RPI; ++q) {
+            const int row = q * RPI + lane / LPR;
+            const uint4 v = *reinterpret_cast<const uint4*>(ep + row * EP_PITCH + (lane % LPR) * 16);
+            const int r = wrow0 + i3 * 32 + hh * 16 + row;
+            if (r < row_end) *reinterpret_cast<uint4*>(p.out + (int64_t)r * p.ldo + out_col) = v;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   }
 }

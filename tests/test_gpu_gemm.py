@@ -65,7 +65,7 @@ def routing(rng, T, topk, E, skew=False):
 
 
 def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
-              exact=False, layout=0, a_layout=0):
+              exact=False, layout=0, a_layout=0, with_f32=True):
     rng = np.random.default_rng(seed)
     Et = E + ns
     k = topk + ns
@@ -120,7 +120,8 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
         a_kw = dict(a=dev(cc), a_scale=dev(cs), afmt=gpu_lib.A_MXFP4)
         gather = {}
     n_out = N // 2 if stage == 1 else N
-    out_f32 = torch.full((T * k, n_out), float("nan"), dtype=torch.float32, device="cuda")
+    out_f32 = (torch.full((T * k, n_out), float("nan"), dtype=torch.float32, device="cuda")
+               if with_f32 else None)
     afmt_code = a_kw.pop("afmt")
     wkw = gpu_weight_args(wd, wfmt)
     if layout == gpu_lib.LAYOUT_FRAGMENT:
@@ -134,6 +135,9 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
     ref_unrounded = OG.grouped_stage(stage, a_sorted, perm_ref["expert_offsets"],
                                      lambda e: oracle_weight(wd, wfmt, e), rounding=False)
     g_bits = bits_of(out)[:n_rows]
+    if not with_f32:
+        assert_bf16_close(g_bits, ref_unrounded, f"stage{stage} {wfmt}/{afmt} bf16 only")
+        return
     g_f32 = host(out_f32)[:n_rows]
     if exact:
         assert np.array_equal(g_f32.astype(np.float64), ref_unrounded), "exact special case"
@@ -210,6 +214,16 @@ def test_mx_gemm_wide_tiles(gpu_lib, case):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
     run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
               layout=gpu_lib.LAYOUT_FRAGMENT)
+
+
+@pytest.mark.parametrize("a_layout", [0, 1])
+@pytest.mark.parametrize("case", WIDE_CASES)
+def test_mx_gemm_wide_tiles_bf16_only(gpu_lib, case, a_layout):
+    """Without the fp32 copy the 192 x 512 tiles write bf16 rows through LDS
+    with 16-byte stores."""
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=a_layout, with_f32=False)
 
 
 @pytest.mark.parametrize("case", [c for c in MX_CASES + WIDE_CASES if c[1] == "mx" and c[8] >= 128])
