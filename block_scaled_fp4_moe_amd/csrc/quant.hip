@@ -10,9 +10,9 @@
 // quantize-dequantize round trip before each GEMM; every step is an IEEE
 // float32 operation with round-to-nearest-even.
 //
-// Layout: each lane owns 8 consecutive bf16 (one 16-byte load), so 4 lanes
-// cover an MX block and 2 lanes an NVFP4 block; block maxima are combined
-// with xor shuffles.  Loads and stores are 16 B per lane, fully coalesced.
+// Layout: mxfp4_quant_1x32 gives each lane one whole 32-value block; in
+// nvfp4_qdq each lane owns 8 consecutive bf16 (one 16-byte load), 2 lanes an
+// NVFP4 block, with block maxima combined by xor shuffles.
 #include "common.h"
 
 namespace fp4moe {
@@ -66,6 +66,9 @@ __device__ __forceinline__ float e4m3_rne_sat(float v, uint32_t* code) {
 
 // ---- mxfp4_quant_1x32 ---------------------------------------------------
 
+// One lane per 32-value block: four 16-byte loads, the block maximum without
+// cross-lane traffic, one 16-byte code store and one scale byte per output
+// row.
 // CHUNKED: output in the chunk-major layout, byte (c*out_rows + o)*64 +
 // (k%128)/2 for codes and (c*out_rows + o)*4 + (k%128)/32 for scales
 // (c = k/128), with output rows o = row_map[row*map_k + j] (entries outside
@@ -77,55 +80,58 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(
     const int32_t* __restrict__ row_map, int map_k, int out_rows,
     const int32_t* __restrict__ row_count, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
-  const int chunks_per_row = K / 8;
-  const int64_t total = (int64_t)M * chunks_per_row;
+  const int bpr = K / 32;                           // blocks per row
   const int rows = row_count ? min(M, *row_count) : M;
+  const int64_t total = (int64_t)rows * bpr;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c - threadIdx.x % 4 < total;
-       c += stride) {
-    const int64_t row = c / chunks_per_row;
-    const int cr = (int)(c - row * chunks_per_row);
-    const bool active = c < total && row < rows;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (active) {
-      const int64_t src = gather ? (int64_t)gather[row] : row;
-      v = *reinterpret_cast<const uint4*>(x + src * ldx + (int64_t)cr * 8);
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+    const int64_t row = t / bpr;
+    const int b = (int)(t - row * bpr);
+    const int64_t src = gather ? (int64_t)gather[row] : row;
+    const uint4* xp = reinterpret_cast<const uint4*>(x + src * ldx + (int64_t)b * 32);
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xp[q];
+      w[4 * q] = v.x;
+      w[4 * q + 1] = v.y;
+      w[4 * q + 2] = v.z;
+      w[4 * q + 3] = v.w;
     }
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t amax = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
       amax = max(amax, w[i] & 0x7fffu);
       amax = max(amax, (w[i] >> 16) & 0x7fffu);
     }
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
     const int f = (int)(amax >> 7);                 // bf16 biased exponent of amax
     const uint32_t sbyte = (uint32_t)max(f - 2, 0);
     const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^(127 - sbyte) = 2^-e
-    uint32_t packed = 0;
+    uint32_t packed[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
-      const float q = bf16_to_f32(h & 0x7fffu) * inv;
-      const uint32_t code = e2m1_mag_code(q) | ((h >> 12) & 8u);
-      packed |= code << (4 * i);
-    }
-    if (active) {
-      if (CHUNKED) {
-        // 16 lanes of 8 values per 128-wide chunk; one copy per mapped row
-        const int n_dst = row_map ? map_k : 1;
-        for (int j = 0; j < n_dst; ++j) {
-          const int64_t o = row_map ? (int64_t)row_map[row * map_k + j] : row;
-          if (o < 0 || o >= out_rows) continue;
-          const int64_t slab = (int64_t)(cr >> 4) * out_rows + o;
-          *reinterpret_cast<uint32_t*>(codes + slab * 64 + (cr & 15) * 4) = packed;
-          if ((cr & 3) == 0) scales[slab * 4 + ((cr & 15) >> 2)] = (uint8_t)sbyte;
-        }
-      } else {
-        *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + (int64_t)cr * 4) = packed;
-        if ((cr & 3) == 0) scales[row * (K / 32) + cr / 4] = (uint8_t)sbyte;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t h = (w[4 * d + (i >> 1)] >> (16 * (i & 1))) & 0xffffu;
+        const float q = bf16_to_f32(h & 0x7fffu) * inv;
+        word |= (e2m1_mag_code(q) | ((h >> 12) & 8u)) << (4 * i);
       }
+      packed[d] = word;
+    }
+    const uint4 cv = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (CHUNKED) {
+      const int n_dst = row_map ? map_k : 1;
+      for (int j = 0; j < n_dst; ++j) {
+        const int64_t o = row_map ? (int64_t)row_map[row * map_k + j] : row;
+        if (o < 0 || o >= out_rows) continue;
+        const int64_t slab = (int64_t)(b >> 2) * out_rows + o;
+        *reinterpret_cast<uint4*>(codes + slab * 64 + (b & 3) * 16) = cv;
+        scales[slab * 4 + (b & 3)] = (uint8_t)sbyte;
+      }
+    } else {
+      *reinterpret_cast<uint4*>(codes + row * (K / 2) + (int64_t)b * 16) = cv;
+      scales[row * bpr + b] = (uint8_t)sbyte;
     }
   }
 }
@@ -232,11 +238,11 @@ extern "C" int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx,
   FP4MOE_REQUIRE(ldx >= K && ldx % 8 == 0, "mxfp4_quant_1x32: ldx=%lld", (long long)ldx);
   if (M == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(x && codes && scales, "mxfp4_quant_1x32: null pointer");
-  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 3) == 0,
-                 "mxfp4_quant_1x32: x must be 16-byte and codes 4-byte aligned");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 15) == 0,
+                 "mxfp4_quant_1x32: x and codes must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
-  const int64_t chunks = (int64_t)M * (K / 8);
-  hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3(grid_for(chunks, 256)), dim3(256), 0,
+  const int64_t blocks = (int64_t)M * (K / 32);
+  hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3(grid_for(blocks, 256)), dim3(256), 0,
                      as_stream(stream), x, M, K, ldx, row_gather, nullptr, 1, M, row_count, codes,
                      scales);
   return check_launch("mxfp4_quant_1x32");
@@ -254,11 +260,11 @@ extern "C" int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t
   FP4MOE_REQUIRE(out_rows >= 0, "mxfp4_quant_1x32_chunked: out_rows=%d", out_rows);
   if (M == 0 || out_rows == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(x && codes && scales, "mxfp4_quant_1x32_chunked: null pointer");
-  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 3) == 0,
-                 "mxfp4_quant_1x32_chunked: x must be 16-byte and codes 4-byte aligned");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 15) == 0,
+                 "mxfp4_quant_1x32_chunked: x and codes must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
-  const int64_t chunks = (int64_t)M * (K / 8);
-  hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3(grid_for(chunks, 256)), dim3(256), 0,
+  const int64_t blocks = (int64_t)M * (K / 32);
+  hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3(grid_for(blocks, 256)), dim3(256), 0,
                      as_stream(stream), x, M, K, ldx, nullptr, row_map, map_k, out_rows,
                      row_count, codes, scales);
   return check_launch("mxfp4_quant_1x32_chunked");

@@ -136,7 +136,8 @@ int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int n_shared, i
  * x bf16 with row stride ldx (elements); output row r reads input row
  * row_gather[r] when row_gather != NULL.  row_count (device, NULL = M) limits
  * the rows processed; rows at or past it are not written.
- * -> codes uint8 [M, K/2], scales uint8 [M, K/32].  K % 32 == 0.
+ * -> codes uint8 [M, K/2], scales uint8 [M, K/32].  K % 32 == 0; x and
+ * codes 16-byte aligned, ldx % 8 == 0.
  */
 int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx, const int32_t* row_gather,
                      const int32_t* row_count, uint8_t* codes, uint8_t* scales, void* stream);
@@ -154,7 +155,7 @@ int mxfp4_quant_1x32(const uint16_t* x, int M, int K, int64_t ldx, const int32_t
  * codes land in expert order; entries outside [0, out_rows) are skipped),
  * else to output row r (out_rows >= M).  Rows no input maps to are not
  * written.  K % 128 == 0.  codes [K/128, out_rows, 64], scales
- * [K/128, out_rows, 4].
+ * [K/128, out_rows, 4]; x and codes 16-byte aligned, ldx % 8 == 0.
  */
 int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t ldx, const int32_t* row_map,
                              int map_k, int out_rows, const int32_t* row_count, uint8_t* codes,
