@@ -32,7 +32,9 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a, "fp4_grouped_gemm: null args");
   FP4MOE_REQUIRE(a->stage == 1 || a->stage == 2, "fp4_grouped_gemm: stage=%d", a->stage);
   const bool mx = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_MXFP4;
-  const bool dq = !mx;
+  // FP8 weights x MXFP4 activations on the scaled MFMA: 192-row tiles
+  const bool mx8 = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_FP8 && a->block_m == 192;
+  const bool dq = !mx && !mx8;
   FP4MOE_REQUIRE(a->afmt == FP4MOE_A_BF16 || a->afmt == FP4MOE_A_MXFP4,
                  "fp4_grouped_gemm: afmt=%d", a->afmt);
   FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4 || a->wfmt == FP4MOE_W_FP8,
@@ -46,6 +48,13 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
     FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64,
                    "fp4_grouped_gemm: block_m=%d not in {16,32,64} for this format pair",
                    a->block_m);
+  } else if (mx8) {
+    FP4MOE_REQUIRE(a->w_layout == FP4MOE_LAYOUT_FRAGMENT,
+                   "fp4_grouped_gemm: block_m 192 needs fragment-major weights");
+    const int n_out = a->stage == 1 ? a->N / 2 : a->N;
+    const int out_per_wg = a->stage == 1 ? 128 : 256;
+    FP4MOE_REQUIRE(n_out % out_per_wg == 0,
+                   "fp4_grouped_gemm: output width %d not a multiple of %d", n_out, out_per_wg);
   } else {
     FP4MOE_REQUIRE(a->block_m == 32 || a->block_m == 64 || a->block_m == 128 ||
                        a->block_m == 192 || a->block_m == 256,
@@ -70,21 +79,26 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a->a_layout == FP4MOE_A_LAYOUT_ROWMAJOR || a->a_layout == FP4MOE_A_LAYOUT_CHUNKED,
                  "fp4_grouped_gemm: a_layout=%d", a->a_layout);
   const bool a_chunked = a->a_layout == FP4MOE_A_LAYOUT_CHUNKED;
-  FP4MOE_REQUIRE(!a_chunked || (mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
-                                (a->block_m == 128 || a->block_m == 192 || a->block_m == 256)),
-                 "fp4_grouped_gemm: chunked activations need MXFP4 x MXFP4, fragment weights "
-                 "and block_m 128, 192 or 256");
+  FP4MOE_REQUIRE(!a_chunked || mx8 ||
+                     (mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
+                      (a->block_m == 128 || a->block_m == 192 || a->block_m == 256)),
+                 "fp4_grouped_gemm: chunked activations need MXFP4 activations, fragment "
+                 "weights and block_m 128, 192 or 256 (FP8 weights: 192)");
   FP4MOE_REQUIRE(!a_chunked || (a->a_rows >= 1 && a->a_rows <= (1 << 26) &&
                                 (a->a_row_gather || a->a_rows >= a->max_rows)),
                  "fp4_grouped_gemm: a_rows=%d (max_rows=%d)", a->a_rows, a->max_rows);
   // the LDS-DMA tiles (MXFP4 x MXFP4, fragment weights, block_m >= 128) address
   // row-major A rows with 32-bit byte offsets
-  FP4MOE_REQUIRE(!(mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT && a->block_m >= 128 && !a_chunked) ||
+  FP4MOE_REQUIRE(!((mx || mx8) && a->w_layout == FP4MOE_LAYOUT_FRAGMENT && a->block_m >= 128 &&
+                   !a_chunked) ||
                      (int64_t)a->max_rows * (a->lda / 2) <= (int64_t)0xffffffff,
                  "fp4_grouped_gemm: row-major A of %d rows x lda %lld exceeds 4 GiB for block_m %d",
                  a->max_rows, (long long)a->lda, a->block_m);
   const int n_out = a->stage == 1 ? a->N / 2 : a->N;
   FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
+  // the 192-row tiles store 16-byte pieces of output rows
+  FP4MOE_REQUIRE(a->block_m != 192 || (a->ldo % 8 == 0 && ((uintptr_t)a->out & 15) == 0),
+                 "fp4_grouped_gemm: block_m 192 needs ldo %% 8 == 0 and a 16-byte aligned out");
   FP4MOE_REQUIRE(a_chunked || (a->lda >= a->K && a->lda % 32 == 0), "fp4_grouped_gemm: lda=%lld",
                  (long long)a->lda);
   if (a->max_tiles == 0 || a->max_rows == 0) return FP4MOE_OK;
@@ -128,6 +142,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   const int mt = a->max_tiles;
   const int st = a->stage;
   if (mx) launch_mx_gemm(p, st, mt, s);
+  else if (mx8) launch_mx_fp8_wide_gemm(p, st, mt, s);
   else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");

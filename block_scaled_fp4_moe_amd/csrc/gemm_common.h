@@ -170,6 +170,8 @@ int grid_cap();
 void launch_dq_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
                     hipStream_t s);
 void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+// FP8 weights x MXFP4 activations on the scaled MFMA (block_m 192, fragment weights).
+void launch_mx_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
 // Tiled dq variant (64-row tiles, fragment weights): whether it takes `p`.
 bool dqt_supported(const GemmParams& p, int stage);
 void launch_dqt_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,

@@ -643,7 +643,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 }
 
 // ---------------------------------------------------------------------------
-// mx family, wide tiles (block_m 192): 192 rows x 512 weight rows.
+// mx family, wide tiles (block_m 192): 192 rows x 512 weight rows (MXFP4
+// weights) or x 256 weight rows (FP8 E4M3 weights with a per-row fp32 scale).
 //
 // At prefill sizes every weight byte comes from HBM once, while the
 // activation rows of an expert are copied again for every column block of
@@ -662,6 +663,14 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, WAVES_M * WAVES_N / 4) void
 // fragment and one 64-row scale copy (wave 7 repeats wave 6's scale copy:
 // the same bytes to the same LDS addresses), then 4 weight fragments and
 // their scales.
+// W8: the weights are FP8 E4M3 fragments (16 rows x 128 K = 2 KiB, the two
+// 16-value halves of every 32-value block 1 KiB apart) and enter the same
+// scaled MFMA as format 0 (E2M1 activations stay format 4: the FP4 x FP8
+// rate) with unit block scales; the per-row channel scale
+// multiplies the accumulators in the epilogue.  The tile is 192 x 256 (4 x 64
+// per wave in N, 3 x 2 MFMA tiles), so a stage holds activation codes and
+// scales plus 32 KiB of weights; 6 DMA instructions per wave per chunk
+// (4 for two 2 KiB weight fragments).
 // LDS-DMA with a wave-uniform 64-bit base in scalar registers and a 32-bit
 // per-lane byte offset (the saddr form): one VGPR per address instead of two.
 __device__ __forceinline__ void dma_b128_s(const void* base, uint32_t voff, uint32_t lds) {
@@ -673,19 +682,21 @@ __device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, uint3
                :: "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-template <int STAGE>
+template <int STAGE, bool W8>
 __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) {
   constexpr int S = 3, NW = 8, BM = 192;
   constexpr int WM = 6, MT = 3;                     // 16-row blocks / 32-row tiles per wave
-  constexpr int WN = 8, NT = 4;                     // weight groups / 32-row tiles per wave
-  constexpr int NG_WG = 32, GPW = 4;                // weight groups per workgroup / per copying wave
+  constexpr int WN = W8 ? 4 : 8, NT = WN / 2;       // weight groups / 32-row tiles per wave
+  constexpr int NG_WG = 4 * WN;                     // weight groups per workgroup
+  constexpr int GPW = NG_WG / NW;                   // weight groups copied per wave
+  constexpr int GB = W8 ? 2048 : 1024;              // bytes of one weight fragment
   constexpr int OUT_PER_WAVE = (STAGE == 1) ? (WN / 2) * 16 : WN * 16;
   constexpr int OUT_PER_WG = 4 * OUT_PER_WAVE;
   constexpr int OFF_AS = BM * 64;                   // A codes: [12 blocks][64 lanes][16 B]
   constexpr int OFF_B = OFF_AS + BM * 4;            // A scales: [row][4 blocks]
-  constexpr int OFF_BS = OFF_B + NG_WG * 1024;      // B codes: [32 groups][64 lanes][16 B]
-  constexpr int STAGE_BYTES = OFF_BS + NW * 256;    // B scales: [8 waves][4 groups][64 B]
-  constexpr int D = 7;                              // DMA instructions per wave per chunk
+  constexpr int OFF_BS = OFF_B + NG_WG * GB;        // B fragments: [NG_WG groups][GB]
+  constexpr int STAGE_BYTES = OFF_BS + (W8 ? 0 : NW * 256);   // B scales: [8 waves][4 groups][64 B]
+  constexpr int D = 2 + GPW * (GB / 1024) + (W8 ? 0 : 1);    // DMA instructions per wave per chunk
   constexpr int EP_TILES = (STAGE == 1) ? NT / 2 : NT;   // 32-column output tiles per wave
   constexpr int EP_COLS = 32 * EP_TILES;            // output columns per wave
   constexpr int EP_PITCH = EP_COLS * 2 + 64;        // epilogue LDS row: bf16 + bank skew
@@ -724,7 +735,13 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   const int frag_lane = m16 * 1024 + (lane & 15) * 16 + kb * 256;
   const int a_lds = wm * WM * 1024 + frag_lane;
   const int as_lds = OFF_AS + wm * WM * 64 + (lane & 31) * 4 + kb;
-  const int b_lds = OFF_B + frag_lane;
+  // E4M3 operands of the 32x32x64 MFMA pair with E2M1 ones differently (read
+  // on the device): with lane half kb of the E2M1 operand holding 32-value
+  // block 2h+kb of K step h, lane half kb of the E4M3 operand holds 16-value
+  // half kb of block 2h in its first 16 bytes and half kb of block 2h+1 in
+  // its last 16 bytes.  In the fragment those halves sit at byte
+  // kb*1024 + (row + 16*block)*16.
+  const int b_lds = OFF_B + m16 * GB + (lane & 15) * 16 + (W8 ? kb * 1024 : kb * 256);
   const int bs_lds = OFF_BS + m16 * 64 + (lane & 15) + 16 * kb;
 
   for (int64_t wi = w_begin + slot; wi < w_end; wi += slots) {
@@ -757,8 +774,8 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       else
         grp0 = nb * NG_WG + j0;
     }
-    const uint8_t* b_base = p.w + ((int64_t)e * G + grp0) * nkc * 1024;
-    const uint8_t* bs_base = p.w_scale + ((int64_t)e * nkc * G + grp0) * 64;
+    const uint8_t* b_base = p.w + ((int64_t)e * G + grp0) * nkc * GB;
+    const uint8_t* bs_base = W8 ? nullptr : p.w_scale + ((int64_t)e * nkc * G + grp0) * 64;
 
     auto issue = [&](int c) {
       const uint32_t st = smem_base + (uint32_t)((c % S) * STAGE_BYTES);
@@ -772,8 +789,11 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       }
 #pragma unroll
       for (int q = 0; q < GPW; ++q)
-        dma_b128_s(b_base + ((int64_t)q * nkc + c) * 1024, lane * 16, st + OFF_B + (wave * GPW + q) * 1024);
-      dma_b32_s(bs_base + (int64_t)c * G * 64, lane * 4, st + OFF_BS + wave * 256);
+#pragma unroll
+        for (int hb = 0; hb < GB / 1024; ++hb)
+          dma_b128_s(b_base + ((int64_t)q * nkc + c) * GB + hb * 1024, lane * 16,
+                     st + OFF_B + (wave * GPW + q) * GB + hb * 1024);
+      if (!W8) dma_b32_s(bs_base + (int64_t)c * G * 64, lane * 4, st + OFF_BS + wave * 256);
     };
 
     v16f acc[MT][NT];
@@ -784,7 +804,8 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
 
-    v4u bo[NT], ao[MT];
+    // weight operand: FP4 one 16-byte piece (hi unused), FP8 the two halves
+    v4u bo[NT], bo_hi[NT], ao[MT];
     int bso[NT], aso[MT];
     auto read_ops = [&](int c, int h) {
       const uint8_t* st = smem + (c % S) * STAGE_BYTES;
@@ -793,8 +814,13 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
         const int ju = (STAGE == 1)
                            ? ((nt < NT / 2) ? wn * (WN / 2) + nt * 2 : NG_WG / 2 + wn * (WN / 2) + (nt - NT / 2) * 2)
                            : wn * WN + nt * 2;
-        bo[nt] = *reinterpret_cast<const v4u*>(st + b_lds + ju * 1024 + h * 512);
-        bso[nt] = st[bs_lds + (ju / GPW) * 256 + (ju % GPW) * 64 + h * 32];
+        bo[nt] = *reinterpret_cast<const v4u*>(st + b_lds + ju * GB + h * 512);
+        if (W8) {
+          bo_hi[nt] = *reinterpret_cast<const v4u*>(st + b_lds + ju * GB + h * 512 + 256);
+          bso[nt] = 127;
+        } else {
+          bso[nt] = st[bs_lds + (ju / GPW) * 256 + (ju % GPW) * 64 + h * 32];
+        }
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
@@ -808,9 +834,17 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
         const v8i af = v8i{(int)ao[i][0], (int)ao[i][1], (int)ao[i][2], (int)ao[i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3], 0, 0, 0, 0};
-          acc[i][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][nt], 4, 4, 0,
-                                                                      aso[i], 0, bso[nt]);
+          if (W8) {
+            // A format 4 (E2M1), B format 0 (E4M3)
+            const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3],
+                               (int)bo_hi[nt][0], (int)bo_hi[nt][1], (int)bo_hi[nt][2], (int)bo_hi[nt][3]};
+            acc[i][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][nt], 4, 0, 0,
+                                                                        aso[i], 0, 127);
+          } else {
+            const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3], 0, 0, 0, 0};
+            acc[i][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][nt], 4, 4, 0,
+                                                                        aso[i], 0, bso[nt]);
+          }
         }
       }
     };
@@ -832,23 +866,38 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       for (int h = 0; h < 2; ++h) {
         if (h == 0) wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));
         wait_lgkm0();
-        asm volatile("s_barrier"
-                     : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
-                       "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]),
-                       "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[2][2]), "+v"(acc[2][3])
-                     :
-                     : "memory");
+        if constexpr (W8)
+          asm volatile("s_barrier"
+                       : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                         "+v"(acc[2][0]), "+v"(acc[2][1])
+                       :
+                       : "memory");
+        else
+          asm volatile("s_barrier"
+                       : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]),
+                         "+v"(acc[1][0]), "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3]),
+                         "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[2][2]), "+v"(acc[2][3])
+                       :
+                       : "memory");
         if (h == 0 && c + S - 1 < nkc) issue(c + S - 1);
         read_ops(c, h);
         if (h == 1 && grp == 1 && c + 1 < nkc) wait_chunks<D, S - 2>(min(S - 2, nkc - 2 - c));
         wait_lgkm0();
-        asm volatile("s_barrier"
-                     : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo[2]), "+v"(bo[3]),
-                       "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]),
-                       "+v"(bso[0]), "+v"(bso[1]), "+v"(bso[2]), "+v"(bso[3]),
-                       "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[2])
-                     :
-                     : "memory");
+        if constexpr (W8)
+          asm volatile("s_barrier"
+                       : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo_hi[0]), "+v"(bo_hi[1]),
+                         "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]),
+                         "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[2])
+                       :
+                       : "memory");
+        else
+          asm volatile("s_barrier"
+                       : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo[2]), "+v"(bo[3]),
+                         "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]),
+                         "+v"(bso[0]), "+v"(bso[1]), "+v"(bso[2]), "+v"(bso[3]),
+                         "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[2])
+                       :
+                       : "memory");
         mma();
       }
     }
@@ -858,6 +907,21 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
     // epilogue: lane l holds column l % 32 of each 32x32 tile and rows
     // (i / 4) * 8 + (l / 32) * 4 + i % 4 in accumulator element i
     const int wrow0 = tile_row0 + wm * WM * 16;
+    if constexpr (W8) {
+      // per-row channel scales of the weight rows of this lane's columns
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int gbase = (STAGE == 1)
+                              ? ((nt < NT / 2) ? nb * (NG_WG / 2) + wn * (WN / 2) + nt * 2
+                                               : G / 2 + nb * (NG_WG / 2) + wn * (WN / 2) + (nt - NT / 2) * 2)
+                              : nb * NG_WG + wn * WN + nt * 2;
+        const float cs = p.w_channel_scale[(int64_t)e * p.N + gbase * 16 + (lane & 31)];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) acc[i][nt][k] *= cs;
+      }
+    }
     if (p.out_f32) {
       // fp32 copy requested: element-wise stores of both outputs
       const int col0 = nb * OUT_PER_WG + wn * OUT_PER_WAVE + (lane & 31);
@@ -929,14 +993,14 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   }
 }
 
-template <int STAGE>
+template <int STAGE, bool W8>
 static void launch_mx_wide(const GemmParams& p, int max_tiles, hipStream_t s) {
-  const int out_per_wg = (STAGE == 1) ? 256 : 512;
+  const int out_per_wg = ((STAGE == 1) ? 256 : 512) / (W8 ? 2 : 1);
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
   const int cap = grid_cap() / 8;        // one workgroup (eight waves) per CU
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((mx_dma_wide_gemm_kernel<STAGE>), dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((mx_dma_wide_gemm_kernel<STAGE, W8>), dim3(grid), dim3(512), 0, s, p);
 }
 
 template <int STAGE, int WM>
@@ -980,7 +1044,7 @@ static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
       if (frag) launch_mx_dma<STAGE, 4, 2, 2, 4>(p, max_tiles, s);
       else launch_mx_lds<STAGE, 4>(p, max_tiles, s);
       break;
-    case 192: launch_mx_wide<STAGE>(p, max_tiles, s); break;   // fragment weights only
+    case 192: launch_mx_wide<STAGE, false>(p, max_tiles, s); break;   // fragment weights only
     default:
       if (frag) launch_mx_dma<STAGE, 4, 4, 2, 4>(p, max_tiles, s);
       else launch_mx_lds<STAGE, 8>(p, max_tiles, s);
@@ -991,6 +1055,11 @@ static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
 void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
   if (stage == 1) launch_mx<1>(p, max_tiles, s);
   else launch_mx<2>(p, max_tiles, s);
+}
+
+void launch_mx_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
+  if (stage == 1) launch_mx_wide<1, true>(p, max_tiles, s);
+  else launch_mx_wide<2, true>(p, max_tiles, s);
 }
 
 }  // namespace fp4moe

@@ -59,12 +59,13 @@ class MoELayer:
                 if cfg.wfmt != "fp8":
                     weights[name + "_scale"] = s
         self.w = weights
-        # Prefill tiles (block_m 128 / 192 / 256, MXFP4 x MXFP4, fragment weights)
-        # take their activations chunk-major and already in expert order (the
-        # stage-1 quantizer writes each token to its pairs' sorted rows), so
-        # every tile copy is contiguous.
-        self.chunked = (cfg.afmt == "mx" and cfg.wfmt == "mx" and cfg.fragment_layout
-                        and cfg.block_m in (128, 192, 256))
+        # Prefill tiles (MXFP4 activations, fragment weights; block_m 128 / 192 /
+        # 256 for MXFP4 weights, 192 for FP8 weights) take their activations
+        # chunk-major and already in expert order (the stage-1 quantizer writes
+        # each token to its pairs' sorted rows), so every tile copy is contiguous.
+        self.chunked = (cfg.afmt == "mx" and cfg.fragment_layout and
+                        ((cfg.wfmt == "mx" and cfg.block_m in (128, 192, 256)) or
+                         (cfg.wfmt == "fp8" and cfg.block_m == 192)))
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)

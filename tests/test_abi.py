@@ -118,6 +118,16 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**wide, stage=2, max_tiles=0)[0] == 0
     assert run(**wide, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
     assert run(**{**wide, "block_m": 160})[0] == 1
+    assert run(**{**wide, "ldo": 516}, max_tiles=0)[0] == 1     # 16-byte row stores
+    # FP8 weights x MXFP4 activations at block_m 192 (192 x 256 tiles)
+    wide8 = dict(wfmt=2, afmt=1, block_m=192, w_layout=1, N=256, ldo=256)
+    assert run(**wide8, max_tiles=0)[0] == 0
+    assert run(**wide8, stage=2, max_tiles=0)[0] == 0
+    assert run(**wide8, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
+    assert run(**{**wide8, "w_layout": 0}, max_tiles=0)[0] == 1
+    assert run(**{**wide8, "N": 320}, max_tiles=0)[0] == 1       # output width 160
+    assert run(**{**wide8, "N": 128}, stage=2, max_tiles=0)[0] == 1
+    assert run(**{**wide8, "afmt": 0}, max_tiles=0)[0] == 1      # bf16 activations: 16/32/64
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 
 

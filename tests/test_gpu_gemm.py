@@ -198,6 +198,11 @@ WIDE_CASES = [
     (2, "mx", 300, 8, 8, 1, 1024, 512, 192, 40, False),
     (1, "mx", 100, 2, 4, 0, 128, 256, 192, 41, False),
     (2, "mx", 100, 2, 4, 0, 512, 128, 192, 42, False),
+    # FP8 weights x MXFP4 activations on the scaled MFMA: 192 x 256 tiles
+    (1, "fp8", 400, 4, 8, 1, 512, 256, 192, 43, True),
+    (2, "fp8", 400, 4, 8, 1, 512, 256, 192, 44, True),
+    (1, "fp8", 300, 8, 8, 1, 1024, 128, 192, 45, False),
+    (2, "fp8", 100, 2, 4, 0, 256, 128, 192, 46, False),
 ]
 
 
@@ -226,7 +231,7 @@ def test_mx_gemm_wide_tiles_bf16_only(gpu_lib, case, a_layout):
               layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=a_layout, with_f32=False)
 
 
-@pytest.mark.parametrize("case", [c for c in MX_CASES + WIDE_CASES if c[1] == "mx" and c[8] >= 128])
+@pytest.mark.parametrize("case", [c for c in MX_CASES if c[1] == "mx" and c[8] >= 128] + WIDE_CASES)
 def test_mx_gemm_chunked_activations(gpu_lib, case):
     """Prefill tiles reading chunk-major, pre-gathered MXFP4 activations."""
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case

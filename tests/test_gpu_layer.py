@@ -141,6 +141,6 @@ def test_layer_nvfp4_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", block_m)
 
 
-@pytest.mark.parametrize("block_m", [32, 64])
+@pytest.mark.parametrize("block_m", [32, 64, 192])
 def test_layer_fp8_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", block_m)
