@@ -7,7 +7,7 @@
 // normal with exponent in [-5, 7].
 //
 // The kernel is integer-only.  One wavefront converts one row in two passes
-// over its 16-byte blocks (one MX block per lane per step):
+// over its blocks (all of the row's codes held in registers):
 //   pass 1: the largest element exponent of a block is its E8M0 exponent plus
 //           the exponent class of its largest E2M1 magnitude, found with a few
 //           bit tests on the packed nibbles; a wavefront max gives e_max.
@@ -19,6 +19,7 @@
 namespace fp4moe {
 
 constexpr int kNoElement = -100000;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Exponent class of the largest magnitude among the 8 nibbles of each word:
 // codes 6,7 -> 2; 4,5 -> 1; 2,3 -> 0; 1 -> -1; none -> kNoElement.
@@ -33,6 +34,11 @@ __device__ __forceinline__ int block_max_class(uint32_t w0, uint32_t w1, uint32_
   if (any & 0x22222222u) return 0;
   if (any & 0x11111111u) return -1;
   return kNoElement;
+}
+
+// The same for half a block (16 nibbles in two words).
+__device__ __forceinline__ int half_max_class(uint32_t w0, uint32_t w1) {
+  return block_max_class(w0, w1, 0u, 0u);
 }
 
 // FP8 byte of the E2M1 magnitude code c (1..7) scaled by 2^d, with flags.
@@ -58,6 +64,66 @@ __device__ __forceinline__ uint32_t fp8_of_mag(int c, int d, bool* inexact, bool
 
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
+// Encode 16 values of a block (codes w0, w1; E8M0 byte s, d = s - 127 - k)
+// into 16 FP8 bytes; sets the below / inexact flags for elements that need
+// them.  Every value with magnitude code c maps to the same byte (sign
+// aside), so an 8-entry byte table is built once and applied to 4 nibbles
+// per v_perm_b32.
+__device__ __forceinline__ uint4 encode_half(uint32_t w0, uint32_t w1, int s, int k,
+                                             bool* any_below, bool* any_inexact) {
+  const int d = s - 127 - k;
+  uint32_t lut_lo = 0, lut_hi = 0;
+  uint32_t below_mask = 0, inexact_mask = 0;
+  if (d >= -4) {
+    // fast path: every class lands on a normal with exponent >= -5, exact
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+      const int cls = (c >> 1) - 1;
+      const uint32_t byte = ((uint32_t)(cls + d + 7) << 3) | ((c & 1) && c > 1 ? 4u : 0u);
+      if (c < 4) lut_lo |= byte << (8 * c);
+      else lut_hi |= byte << (8 * (c - 4));
+    }
+  } else {
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+      bool inex, below;
+      const uint32_t byte = fp8_of_mag(c, d, &inex, &below);
+      if (c < 4) lut_lo |= byte << (8 * c);
+      else lut_hi |= byte << (8 * (c - 4));
+      below_mask |= (below ? 1u : 0u) << c;
+      inexact_mask |= (inex ? 1u : 0u) << c;
+    }
+  }
+  const uint32_t win[2] = {w0, w1};
+  uint32_t out[4];
+  uint32_t present = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    // bytes [b0,b0,b1,b1] and [b2,b2,b3,b3], then keep lo/hi nibble alternately
+    const uint32_t t0 = __builtin_amdgcn_perm(win[i], win[i], 0x01010000u);
+    const uint32_t t1 = __builtin_amdgcn_perm(win[i], win[i], 0x03030202u);
+    const uint32_t x0 = (t0 & 0x000f000fu) | ((t0 >> 4) & 0x0f000f00u);
+    const uint32_t x1 = (t1 & 0x000f000fu) | ((t1 >> 4) & 0x0f000f00u);
+    out[2 * i] = __builtin_amdgcn_perm(lut_hi, lut_lo, x0 & 0x07070707u) |
+                 ((x0 & 0x08080808u) << 4);
+    out[2 * i + 1] = __builtin_amdgcn_perm(lut_hi, lut_lo, x1 & 0x07070707u) |
+                     ((x1 & 0x08080808u) << 4);
+    if (below_mask | inexact_mask) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) present |= 1u << ((win[i] >> (4 * n)) & 7u);
+    }
+  }
+  *any_below |= (present & below_mask) != 0;
+  *any_inexact |= (present & inexact_mask) != 0;
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// One wavefront per row, each lane owning half blocks (16 values: 8 code
+// bytes in, 16 FP8 bytes out), so that every load and store instruction of
+// the wavefront covers one contiguous run.  The row's codes and scales stay
+// in registers between the two passes (NH half blocks per lane,
+// K <= 1024 * NH), and the FP8 bytes are written with streaming stores.
+template <int NH>
 __global__ __launch_bounds__(256) void mx_to_fp8_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ scales,
                                                         int64_t rows, int K,
@@ -68,23 +134,35 @@ __global__ __launch_bounds__(256) void mx_to_fp8_kernel(const uint8_t* __restric
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  const int nblk = K / 32;
+  const int nhalf = K / 16;
   const uint8_t* crow = codes + row * (K / 2);
-  const uint8_t* srow = scales + row * nblk;
+  const uint8_t* srow = scales + row * (K / 32);
   uint8_t* orow = fp8 + row * K;
 
+  uint2 w[NH];
+  int sc[NH];
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    const int hb = lane + 64 * j;
+    sc[j] = 255;
+    w[j] = make_uint2(0, 0);
+    if (hb < nhalf) {
+      sc[j] = srow[hb >> 1];
+      w[j] = *reinterpret_cast<const uint2*>(crow + hb * 8);
+    }
+  }
   // pass 1: e_max over finite blocks
   int emax = kNoElement;
   bool has_nan = false;
-  for (int b = lane; b < nblk; b += 64) {
-    const int s = srow[b];
-    if (s == 255) {
+#pragma unroll
+  for (int j = 0; j < NH; ++j) {
+    if (lane + 64 * j >= nhalf) continue;
+    if (sc[j] == 255) {
       has_nan = true;
       continue;
     }
-    const uint4 w = *reinterpret_cast<const uint4*>(crow + b * 16);
-    const int cls = block_max_class(w.x, w.y, w.z, w.w);
-    if (cls != kNoElement) emax = max(emax, s - 127 + cls);
+    const int cls = half_max_class(w[j].x, w[j].y);
+    if (cls != kNoElement) emax = max(emax, sc[j] - 127 + cls);
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
@@ -93,63 +171,18 @@ __global__ __launch_bounds__(256) void mx_to_fp8_kernel(const uint8_t* __restric
 
   // pass 2: encode
   bool any_below = false, any_inexact = false;
-  for (int b = lane; b < nblk; b += 64) {
-    const int s = srow[b];
-    uint4* dst = reinterpret_cast<uint4*>(orow + b * 32);
-    if (s == 255) {
-      const uint4 nanv = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
-      dst[0] = nanv;
-      dst[1] = nanv;
-      continue;
-    }
-    const uint4 w = *reinterpret_cast<const uint4*>(crow + b * 16);
-    const int d = s - 127 - k;
-    // table bytes 0..7 for magnitude codes 0..7
-    uint32_t lut_lo = 0, lut_hi = 0;
-    uint32_t below_mask = 0, inexact_mask = 0;
-    if (d >= -4) {
-      // fast path: every class lands on a normal with exponent >= -5, exact
 #pragma unroll
-      for (int c = 1; c < 8; ++c) {
-        const int cls = (c >> 1) - 1;
-        const uint32_t byte = ((uint32_t)(cls + d + 7) << 3) | ((c & 1) && c > 1 ? 4u : 0u);
-        if (c < 4) lut_lo |= byte << (8 * c);
-        else lut_hi |= byte << (8 * (c - 4));
-      }
+  for (int j = 0; j < NH; ++j) {
+    const int hb = lane + 64 * j;
+    if (hb >= nhalf) continue;
+    uint4 o;
+    if (sc[j] == 255) {
+      o = make_uint4(0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu);
     } else {
-#pragma unroll
-      for (int c = 1; c < 8; ++c) {
-        bool inex, below;
-        const uint32_t byte = fp8_of_mag(c, d, &inex, &below);
-        if (c < 4) lut_lo |= byte << (8 * c);
-        else lut_hi |= byte << (8 * (c - 4));
-        below_mask |= (below ? 1u : 0u) << c;
-        inexact_mask |= (inex ? 1u : 0u) << c;
-      }
+      o = encode_half(w[j].x, w[j].y, sc[j], k, &any_below, &any_inexact);
     }
-    const uint32_t win[4] = {w.x, w.y, w.z, w.w};
-    uint32_t out[8];
-    uint32_t present = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // bytes [b0,b0,b1,b1] and [b2,b2,b3,b3], then keep lo/hi nibble alternately
-      const uint32_t t0 = __builtin_amdgcn_perm(win[i], win[i], 0x01010000u);
-      const uint32_t t1 = __builtin_amdgcn_perm(win[i], win[i], 0x03030202u);
-      const uint32_t x0 = (t0 & 0x000f000fu) | ((t0 >> 4) & 0x0f000f00u);
-      const uint32_t x1 = (t1 & 0x000f000fu) | ((t1 >> 4) & 0x0f000f00u);
-      out[2 * i] = __builtin_amdgcn_perm(lut_hi, lut_lo, x0 & 0x07070707u) |
-                   ((x0 & 0x08080808u) << 4);
-      out[2 * i + 1] = __builtin_amdgcn_perm(lut_hi, lut_lo, x1 & 0x07070707u) |
-                       ((x1 & 0x08080808u) << 4);
-      if (below_mask | inexact_mask) {
-#pragma unroll
-        for (int n = 0; n < 8; ++n) present |= 1u << ((win[i] >> (4 * n)) & 7u);
-      }
-    }
-    any_below |= (present & below_mask) != 0;
-    any_inexact |= (present & inexact_mask) != 0;
-    dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-    dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+    __builtin_nontemporal_store(u32x4{o.x, o.y, o.z, o.w},
+                                reinterpret_cast<u32x4*>(orow + hb * 16));
   }
   has_nan = __ballot(has_nan) != 0;
   any_below = __ballot(any_below) != 0;
@@ -178,12 +211,23 @@ extern "C" int mxfp4_to_fp8_channel(const uint8_t* codes, const uint8_t* scales,
   FP4MOE_REQUIRE(((uintptr_t)codes & 15) == 0 && ((uintptr_t)fp8 & 15) == 0,
                  "mxfp4_to_fp8_channel: codes and fp8 must be 16-byte aligned");
   FP4MOE_REQUIRE((rows + 3) / 4 < (1ll << 31), "mxfp4_to_fp8_channel: too many rows");
+  FP4MOE_REQUIRE(K <= 2048 * 16, "mxfp4_to_fp8_channel: K=%d above 32768", K);
   FP4MOE_CHECK_DEVICE();
   hipStream_t s = as_stream(stream);
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, n_inexact_rows);
   if (rows > 0) {
-    hipLaunchKernelGGL(mx_to_fp8_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, codes,
-                       scales, rows, K, fp8, channel_scale, row_status, n_inexact_rows);
+    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+    const int nh = (K / 16 + 63) / 64;     // half blocks per lane
+#define FP4MOE_CONVERT(NH)                                                                       \
+  hipLaunchKernelGGL(mx_to_fp8_kernel<NH>, grid, block, 0, s, codes, scales, rows, K, fp8,       \
+                     channel_scale, row_status, n_inexact_rows)
+    if (nh <= 1) FP4MOE_CONVERT(1);
+    else if (nh <= 2) FP4MOE_CONVERT(2);
+    else if (nh <= 4) FP4MOE_CONVERT(4);
+    else if (nh <= 8) FP4MOE_CONVERT(8);
+    else if (nh <= 16) FP4MOE_CONVERT(16);
+    else FP4MOE_CONVERT(32);
+#undef FP4MOE_CONVERT
   }
   return check_launch("mxfp4_to_fp8_channel");
 }

@@ -282,7 +282,7 @@ int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* 
  * zero (k = 0).  n_inexact_rows (device, required) receives the number of
  * rows where some finite element is not reproduced exactly; the call sets it.
  * codes [rows, K/2], scales [rows, K/32] -> fp8 [rows, K], channel_scale
- * float32 [rows].  K % 32 == 0.
+ * float32 [rows].  K % 32 == 0, K <= 32768; codes and fp8 16-byte aligned.
  */
 int mxfp4_to_fp8_channel(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                          uint8_t* fp8, float* channel_scale, uint8_t* row_status,

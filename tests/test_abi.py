@@ -75,6 +75,9 @@ def test_quant_and_convert_reject_bad_K():
     st, msg = _status(lambda lib: lib.mxfp4_to_fp8_channel(None, None, 4, 40, None, None, None,
                                                             None, None))
     assert st == 1
+    st, msg = _status(lambda lib: lib.mxfp4_to_fp8_channel(None, None, 4, 32800, None, None, None,
+                                                            None, None))
+    assert st == 1                              # rows up to 32768 values
     st, msg = _status(lambda lib: lib.moe_combine(None, None, None, 2, 8, 1, 7164, None, None,
                                                    None))
     assert st == 1

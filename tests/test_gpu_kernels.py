@@ -268,7 +268,8 @@ def test_convert_golden_rows(gpu_lib):
 
 @pytest.mark.parametrize("R,K,lo,hi,seed", [(512, 256, 0, 9, 1), (300, 7168, 1, 9, 2),
                                             (700, 2048, 1, 9, 3), (400, 512, 8, 20, 4),
-                                            (64, 4096, 0, 40, 5)])
+                                            (64, 4096, 0, 40, 5), (12, 16384, 1, 9, 6),
+                                            (10, 32768, 1, 12, 7)])
 def test_convert_parity(gpu_lib, R, K, lo, hi, seed):
     g = np.random.default_rng(seed)
     codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
