@@ -7,11 +7,11 @@
 // bf16 weight buffer exists in memory.  [ATOM] "When Is the Scale Applied?":
 // the block scale is absorbed while decoding the weight, before the MFMA.
 //
-// Workgroup: four waves, a tile of 64 rows (four 16-row M blocks) by 16
-// weight groups of 16 rows; wave w owns groups 4w..4w+3 (stage 1: two gate
-// groups and the two up groups of the same output columns) for all 64 rows
-// and the whole K, so every weight element is decoded once per workgroup and
-// no cross-wave reduction is needed.  Every operand of a 128-wide K chunk --
+// Workgroup: NW waves, a tile of 64 rows (four 16-row M blocks) by NW x NGW
+// weight groups of 16 rows; wave w owns NGW groups (stage 1: NGW/2 gate
+// groups and the up groups of the same output columns) for all 64 rows and
+// the whole K, so every weight element is decoded once per workgroup and no
+// cross-wave reduction is needed.  Every operand of a 128-wide K chunk --
 // activation fragments, weight fragments, block scales -- is copied global ->
 // LDS by the LDS-DMA form of the load into a ring of S stages (the same ring
 // protocol as the scaled-FP4 kernel).
@@ -28,10 +28,11 @@
 
 namespace fp4moe {
 
-template <int WFMT, int AFMT, int STAGE, int S>
-__global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
+template <int WFMT, int AFMT, int STAGE, int S, int NGW, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void dqt_gemm_kernel(GemmParams p) {
   constexpr int MB = 4, BM = 64;                      // 16-row M blocks per tile
-  constexpr int NW = 4, NGW = 4, NG = NW * NGW;       // weight groups per wave / tile
+  constexpr int NG = NW * NGW;                        // weight groups per tile
+  constexpr int RUN = NGW / 2;                        // groups per contiguous run (gate | up)
   constexpr int OUT_PER_WAVE = (STAGE == 1) ? (NGW / 2) * 16 : NGW * 16;
   constexpr int OUT_PER_WG = NW * OUT_PER_WAVE;
   constexpr bool AMX = AFMT == FP4MOE_A_MXFP4;
@@ -42,10 +43,15 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
   constexpr int A_BYTES = AMX ? BM * 64 : BM * 256;   // MXFP4 codes | bf16 values
   constexpr int OFF_AS = A_BYTES;                     // MXFP4 activation scales [row][4]
   constexpr int OFF_B = OFF_AS + (AMX ? BM * 4 : 0);
-  constexpr int OFF_BS = OFF_B + NG * WFRAG;          // weight scales: [wave][pair][256 B]
-  constexpr int STAGE_BYTES = OFF_BS + (W8 ? 0 : NW * 512);
-  constexpr int DA = AMX ? 2 : 4;                     // activation copies per wave per chunk
-  constexpr int D = DA + NGW * (W8 ? 2 : 1) + (W8 ? 0 : 2);
+  constexpr int RUN_SB = RUN * 64 * SPB;              // scale bytes of one run per chunk
+  constexpr int SDMA = RUN_SB > 256 ? RUN_SB / 256 : 1;   // dword copies per run
+  constexpr int RS = SDMA * 256;                      // LDS slot of one run's scales
+  constexpr int OFF_BS = OFF_B + NG * WFRAG;          // weight scales: [wave][run][RS]
+  constexpr int STAGE_BYTES = OFF_BS + (W8 ? 0 : NW * 2 * RS);
+  constexpr int DA = AMX ? 2 : 16 / NW;               // activation copies per wave per chunk
+  static_assert(!AMX || NW == 4, "MXFP4 activations: four waves");
+  constexpr int D = DA + NGW * (W8 ? 2 : 1) + (W8 ? 0 : 2 * SDMA);
+  static_assert(RUN_SB >= 256 || RUN_SB == 128, "scale run copy");
   static_assert(D * (S - 2) <= 63, "vmcnt range");
   static_assert(S >= 3 && S * STAGE_BYTES <= 160 * 1024, "LDS");
   __shared__ __attribute__((aligned(16))) uint8_t smem[S * STAGE_BYTES];
@@ -80,11 +86,13 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
     const int tile_row0 = p.offsets[e] + mt * BM;
     const int row_end = min(p.offsets[e + 1], tile_row0 + BM);
 
-    // activation copies of this wave: M block `wave` (bf16: its 4 K blocks;
-    // MXFP4: codes, plus one copy of the tile's 64 scale rows)
+    // activation copies of this wave: bf16 the 16 / NW fragments (M block,
+    // K block) from wave * 16 / NW on, all of M block wave * 4 / NW; MXFP4
+    // (four waves) the codes of M block `wave`, plus one copy of the tile's
+    // 64 scale rows
     int64_t a_src;
     {
-      const int r = tile_row0 + wave * 16 + r16;
+      const int r = tile_row0 + (AMX ? wave : wave * 4 / NW) * 16 + r16;
       int64_t arow = 0;
       if (r < row_end) arow = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
       a_src = AMX ? arow * (p.lda / 2) + g * 16 : arow * p.lda * 2 + g * 16;
@@ -96,22 +104,23 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
       if (r < row_end) arow = p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
       as_src = arow * (p.lda / 32);
     }
-    // this wave's weight groups: pair 0 = q 0,1, pair 1 = q 2,3 (stage 1:
-    // gate pair, up pair), each pair a contiguous run of groups
-    int grp_pair[2];
+    // this wave's weight groups: run 0 = q < RUN, run 1 = q >= RUN (stage 1:
+    // gate run, up run), each a contiguous run of groups in the tensor
+    int grp_run[2];
     if (STAGE == 1) {
-      grp_pair[0] = nb * (NG / 2) + wave * 2;
-      grp_pair[1] = G / 2 + nb * (NG / 2) + wave * 2;
+      grp_run[0] = nb * (NG / 2) + wave * RUN;
+      grp_run[1] = G / 2 + nb * (NG / 2) + wave * RUN;
     } else {
-      grp_pair[0] = nb * NG + wave * 4;
-      grp_pair[1] = grp_pair[0] + 2;
+      grp_run[0] = nb * NG + wave * NGW;
+      grp_run[1] = grp_run[0] + RUN;
     }
-    const int64_t w_pair0 = ((int64_t)e * G + grp_pair[0]) * nkc * WFRAG;
-    const int64_t w_pair1 = ((int64_t)e * G + grp_pair[1]) * nkc * WFRAG;
-    const int64_t s_pair0 = ((int64_t)e * nkc * G + grp_pair[0]) * (64 * SPB);
-    const int64_t s_pair1 = ((int64_t)e * nkc * G + grp_pair[1]) * (64 * SPB);
-    // scale pair copy: MX 128 B (lanes 32..63 repeat 0..31), NVFP4 256 B
-    const uint32_t bs_lane = (SPB == 1) ? (lane & 31) * 4 : lane * 4;
+    const int64_t w_run0 = ((int64_t)e * G + grp_run[0]) * nkc * WFRAG;
+    const int64_t w_run1 = ((int64_t)e * G + grp_run[1]) * nkc * WFRAG;
+    const int64_t s_run0 = ((int64_t)e * nkc * G + grp_run[0]) * (64 * SPB);
+    const int64_t s_run1 = ((int64_t)e * nkc * G + grp_run[1]) * (64 * SPB);
+    // scale run copy: 256-byte dword copies; a 128-byte run (MX, 2 groups)
+    // has lanes 32..63 repeat 0..31
+    const uint32_t bs_lane = (RUN_SB == 128) ? (lane & 31) * 4 : lane * 4;
 
     auto issue = [&](int c) {
       const uint32_t st = smem_base + (uint32_t)((c % S) * STAGE_BYTES);
@@ -120,19 +129,24 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
         dma_b32(p.a_scale + as_src + (int64_t)c * 4, st + OFF_AS);
       } else {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          dma_b128(A + a_src + (int64_t)c * 256 + blk * 64, st + (wave * 4 + blk) * 1024);
+        for (int blk = 0; blk < DA; ++blk) {
+          const int idx = wave * DA + blk;              // fragment (M block idx / 4, K block idx % 4)
+          dma_b128(A + a_src + (int64_t)c * 256 + (idx % 4) * 64, st + idx * 1024);
+        }
       }
 #pragma unroll
       for (int q = 0; q < NGW; ++q) {
-        const int64_t src = ((q < 2) ? w_pair0 : w_pair1) + ((int64_t)(q & 1) * nkc + c) * WFRAG;
+        const int64_t src = ((q < RUN) ? w_run0 : w_run1) + ((int64_t)(q % RUN) * nkc + c) * WFRAG;
         dma_b128(p.w + src + lane * 16, st + OFF_B + (wave * NGW + q) * WFRAG);
         if (W8) dma_b128(p.w + src + 1024 + lane * 16, st + OFF_B + (wave * NGW + q) * WFRAG + 1024);
       }
       if (!W8) {
         const int64_t sstride = (int64_t)c * G * (64 * SPB);
-        dma_b32(p.w_scale + s_pair0 + sstride + bs_lane, st + OFF_BS + wave * 512);
-        dma_b32(p.w_scale + s_pair1 + sstride + bs_lane, st + OFF_BS + wave * 512 + 256);
+#pragma unroll
+        for (int d = 0; d < SDMA; ++d) {
+          dma_b32(p.w_scale + s_run0 + sstride + d * 256 + bs_lane, st + OFF_BS + (wave * 2) * RS + d * 256);
+          dma_b32(p.w_scale + s_run1 + sstride + d * 256 + bs_lane, st + OFF_BS + (wave * 2 + 1) * RS + d * 256);
+        }
       }
     };
 
@@ -159,11 +173,11 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
         wv[q][0] = *reinterpret_cast<const uint4*>(fp);
         if (W8) wv[q][W8 ? 1 : 0] = *reinterpret_cast<const uint4*>(fp + 1024);
         if (WFMT == FP4MOE_W_MXFP4) {
-          const uint32_t b = st[OFF_BS + wave * 512 + (q >> 1) * 256 + (q & 1) * 64 + lane];
+          const uint32_t b = st[OFF_BS + (wave * 2 + q / RUN) * RS + (q % RUN) * 64 + lane];
           sc[q][0] = sc[q][1] = __uint_as_float(b << 23);   // the exponent field is the E8M0 byte
         } else if (WFMT == FP4MOE_W_NVFP4) {
           const uint32_t two = *reinterpret_cast<const uint16_t*>(
-              st + OFF_BS + wave * 512 + (q >> 1) * 256 + (q & 1) * 128 + lane * 2);
+              st + OFF_BS + (wave * 2 + q / RUN) * RS + (q % RUN) * 128 + lane * 2);
           sc[q][0] = e4m3_to_f32(two & 0xffu);
           sc[q][1] = e4m3_to_f32(two >> 8);
         } else {
@@ -209,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
     float cs[NGW];
 #pragma unroll
     for (int q = 0; q < NGW; ++q) {
-      const int wrow = grp_pair[q >> 1] * 16 + (q & 1) * 16 + r16;
+      const int wrow = grp_run[q / RUN] * 16 + (q % RUN) * 16 + r16;
       if (WFMT == FP4MOE_W_NVFP4) cs[q] = p.w_tensor_scale[e];
       else if (WFMT == FP4MOE_W_FP8) cs[q] = p.w_channel_scale[(int64_t)e * p.N + wrow];
       else cs[q] = 1.0f;
@@ -223,8 +237,8 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
         if (r >= row_end) continue;
         if (STAGE == 1) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const float h = silu_mul(acc[mb][j][i] * cs[j], acc[mb][j + 2][i] * cs[j + 2]);
+          for (int j = 0; j < RUN; ++j) {
+            const float h = silu_mul(acc[mb][j][i] * cs[j], acc[mb][j + RUN][i] * cs[j + RUN]);
             const int64_t o = (int64_t)r * p.ldo + col0 + j * 16;
             p.out[o] = (uint16_t)f32_to_bf16_rne(h);
             if (p.out_f32) p.out_f32[o] = h;
@@ -243,21 +257,40 @@ __global__ __launch_bounds__(256, 1) void dqt_gemm_kernel(GemmParams p) {
   }
 }
 
-template <int WFMT, int AFMT, int STAGE>
+template <int WFMT, int AFMT, int STAGE, int NGW, int NW>
 static void launch_dqt_stage(const GemmParams& p, int max_tiles, hipStream_t s) {
-  constexpr int S = (WFMT == FP4MOE_W_FP8 && AFMT == FP4MOE_A_BF16) ? 3 : 4;
-  const int out_per_wg = (STAGE == 1) ? 128 : 256;
+  // 32 groups per tile fit a 3-stage ring; 16 groups a 4-stage ring (3 with
+  // FP8 fragments and bf16 activations)
+  constexpr int S = (NGW * NW == 32 || (WFMT == FP4MOE_W_FP8 && AFMT == FP4MOE_A_BF16)) ? 3 : 4;
+  const int out_per_wg = ((STAGE == 1) ? 8 : 16) * NGW * NW;
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
   const int cap = grid_cap() / 8;        // one workgroup per CU
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((dqt_gemm_kernel<WFMT, AFMT, STAGE, S>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((dqt_gemm_kernel<WFMT, AFMT, STAGE, S, NGW, NW>), dim3(grid), dim3(64 * NW), 0,
+                     s, p);
+}
+
+// FP4 weights with bf16 activations, when the output width allows: eight
+// waves (two per SIMD, so one decodes while the other multiplies) of four
+// groups, a tile 512 weight rows wide (half the activation copies per weight
+// byte).  Otherwise four waves of four groups.
+static bool wide_dqt(int wfmt, int afmt, int stage, int n_out) {
+  return wfmt != FP4MOE_W_FP8 && afmt == FP4MOE_A_BF16 && n_out % (stage == 1 ? 256 : 512) == 0;
 }
 
 template <int WFMT, int AFMT>
 static void launch_dqt_fmt(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
-  if (stage == 1) launch_dqt_stage<WFMT, AFMT, 1>(p, max_tiles, s);
-  else launch_dqt_stage<WFMT, AFMT, 2>(p, max_tiles, s);
+  const int n_out = stage == 1 ? p.N / 2 : p.N;
+  if constexpr (WFMT != FP4MOE_W_FP8 && AFMT == FP4MOE_A_BF16) {
+    if (wide_dqt(WFMT, AFMT, stage, n_out)) {
+      if (stage == 1) launch_dqt_stage<WFMT, AFMT, 1, 4, 8>(p, max_tiles, s);
+      else launch_dqt_stage<WFMT, AFMT, 2, 4, 8>(p, max_tiles, s);
+      return;
+    }
+  }
+  if (stage == 1) launch_dqt_stage<WFMT, AFMT, 1, 4, 4>(p, max_tiles, s);
+  else launch_dqt_stage<WFMT, AFMT, 2, 4, 4>(p, max_tiles, s);
 }
 
 bool dqt_supported(const GemmParams& p, int stage) {
