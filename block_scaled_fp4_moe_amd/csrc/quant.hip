@@ -140,25 +140,42 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(
 
 __global__ void nvfp4_zero_kernel(uint32_t* ws) { ws[0] = 0u; }
 
+// Tensor amax: four independent 16-byte loads in flight per lane per step,
+// one maximum per workgroup (LDS), one atomic per workgroup.
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* __restrict__ x, int M,
                                                          int K, const int32_t* __restrict__ row_count,
                                                          uint32_t* __restrict__ ws) {
+  __shared__ uint32_t wave_max[4];
   const int rows = row_count ? min(M, *row_count) : M;
   const int64_t total = (int64_t)rows * (K / 8);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
   uint32_t amax = 0;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
-       c += (int64_t)gridDim.x * blockDim.x) {
-    const uint4 v = reinterpret_cast<const uint4*>(x)[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int64_t c0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c0 < total; c0 += 4 * stride) {
+    uint4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      amax = max(amax, w[i] & 0x7fffu);
-      amax = max(amax, (w[i] >> 16) & 0x7fffu);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + u * stride;
+      v[u] = c < total ? xv[c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        amax = max(amax, w[i] & 0x7fffu);
+        amax = max(amax, (w[i] >> 16) & 0x7fffu);
+      }
     }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off, 64));
-  if ((threadIdx.x & 63) == 0 && amax) atomicMax(ws, amax);
+  if ((threadIdx.x & 63) == 0) wave_max[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t m = max(max(wave_max[0], wave_max[1]), max(wave_max[2], wave_max[3]));
+    if (m) atomicMax(ws, m);
+  }
 }
 
 __global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
@@ -291,8 +308,11 @@ extern "C" int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_cou
       return set_error(FP4MOE_ERR_WORKSPACE, "nvfp4_qdq: dynamic scale needs %zu bytes",
                        nvfp4_qdq_workspace());
     hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, s, ws);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3(grid_for(chunks, 256 * 8)), dim3(256), 0, s, x, M,
-                       K, row_count, ws);
+    // about 16 chunks per lane, at most 1024 workgroups (atomics)
+    int64_t g = (chunks + 256 * 16 - 1) / (256 * 16);
+    g = g < 1 ? 1 : (g > 1024 ? 1024 : g);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)g), dim3(256), 0, s, x, M, K, row_count,
+                       ws);
   }
   hipLaunchKernelGGL(nvfp4_qdq_kernel, dim3(grid_for(chunks, 256)), dim3(256), 0, s, x, M, K,
                      row_count, tensor_scale_in, ws, y, codes, scales_e4m3, tensor_scale_out);
