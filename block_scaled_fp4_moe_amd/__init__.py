@@ -65,6 +65,7 @@ def load():
         "moe_permute_max_tiles": ([I, I, I, I, I], I),
         "moe_permute_workspace": ([I, I, I, I, I], S),
         "moe_permute": ([P, I, I, I, I, I, P, S, P, P, P, P, P, P, P], I),
+        "moe_route_permute": ([P, P, I, I, I, I, I, I, F, I, I, P, P, P, P, P, P, P, P, P], I),
         "mxfp4_quant_1x32": ([P, I, I, I64, P, P, P, P, P], I),
         "mxfp4_quant_1x32_chunked": ([P, I, I, I64, P, I, I, P, P, P, P], I),
         "nvfp4_qdq_workspace": ([], S),
@@ -155,6 +156,38 @@ def moe_permute(topk_ids, E, n_shared, block_m, workspace=None, out=None, stream
                            _p(out["tiles"]), _p(out["n_tiles"]), _p(out["n_dropped"]),
                            _stream(stream)))
     return out
+
+
+def moe_route_permute(logits, bias, n_group, topk_group, topk, n_shared, block_m,
+                      renormalize=True, routed_scale=1.0, topk_ids=None, topk_w=None, out=None,
+                      stream=None):
+    """moe_route then moe_permute in one launch (T * (topk + n_shared) <= 1024).
+    Returns (topk_ids, topk_w, perm) with perm as moe_permute returns it."""
+    lib = load()
+    T, E = logits.shape
+    assert logits.dtype == torch.float32 and logits.is_contiguous()
+    dev = _dev(logits)
+    k = topk + n_shared
+    if topk_ids is None:
+        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    mt = lib.moe_permute_max_tiles(T, topk, E, n_shared, block_m)
+    if out is None:
+        out = dict(
+            expert_offsets=torch.empty(E + n_shared + 1, dtype=torch.int32, device=dev),
+            sorted_pairs=torch.empty(T * k, dtype=torch.int32, device=dev),
+            pair_pos=torch.empty(T * k, dtype=torch.int32, device=dev),
+            tiles=torch.empty((max(mt, 1), 2), dtype=torch.int32, device=dev),
+            n_tiles=torch.empty(1, dtype=torch.int32, device=dev),
+            n_dropped=torch.empty(1, dtype=torch.int32, device=dev))
+    out["max_tiles"] = mt
+    _check(lib.moe_route_permute(_p(logits), _p(bias), T, E, n_group, topk_group, topk,
+                                 int(bool(renormalize)), float(routed_scale), n_shared, block_m,
+                                 _p(topk_ids), _p(topk_w), _p(out["expert_offsets"]),
+                                 _p(out["sorted_pairs"]), _p(out["pair_pos"]), _p(out["tiles"]),
+                                 _p(out["n_tiles"]), _p(out["n_dropped"]), _stream(stream)))
+    return topk_ids, topk_w, out
 
 
 def mxfp4_quant_1x32(x, row_gather=None, row_count=None, codes=None, scales=None, M=None,

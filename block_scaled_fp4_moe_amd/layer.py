@@ -1,7 +1,8 @@
 """The MoE layer as a chain of the C-ABI calls (marshalling and buffer reuse only).
 
 Order ([ATOM] "Stage D: MXFP4 Fused MoE", [NVFP4] "Weight Dequantization and
-Activation QDQ"): moe_route -> moe_permute -> activation quantization
+Activation QDQ"): moe_route -> moe_permute (one launch, moe_route_permute, at
+decode sizes) -> activation quantization
 (mxfp4_quant_1x32 | nvfp4_qdq | none) -> fp4_grouped_gemm stage 1 (gate/up,
 SiLU*up) -> quantization of h -> fp4_grouped_gemm stage 2 (down) ->
 moe_combine.  Every step is a kernel of libfp4moe; this module only
@@ -14,8 +15,15 @@ import torch
 
 from . import (A_BF16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
                LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle, moe_combine,
-               moe_permute, moe_permute_max_tiles, moe_route, mxfp4_quant_1x32,
+               moe_permute, moe_permute_max_tiles, moe_route, moe_route_permute,
+               mxfp4_quant_1x32,
                mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
+
+
+# moe_route_permute (one launch) takes T * (topk + n_shared) up to 1024 pairs; it
+# measured faster than the two launches only for the smallest batches, where
+# the permutation is one wavefront group.
+ROUTE_PERMUTE_MAX_PAIRS = 64
 
 
 @dataclass
@@ -122,11 +130,19 @@ class MoELayer:
         k = c.topk + c.n_shared
         b = self._buffers(T)
         tick("route")
-        moe_route(logits, bias, c.n_group, c.topk_group, c.topk, c.renormalize, c.routed_scale,
-                  topk_ids=b["topk_ids"], topk_w=b["topk_w"], stream=stream)
-        tick("permute")
-        perm = moe_permute(b["topk_ids"], c.E, c.n_shared, c.block_m, workspace=b["perm_ws"],
-                           out=b["perm"], stream=stream)
+        if T * k <= ROUTE_PERMUTE_MAX_PAIRS:
+            # decode sizes: routing and permutation in one launch
+            _, _, perm = moe_route_permute(logits, bias, c.n_group, c.topk_group, c.topk,
+                                           c.n_shared, c.block_m, c.renormalize, c.routed_scale,
+                                           topk_ids=b["topk_ids"], topk_w=b["topk_w"],
+                                           out=b["perm"], stream=stream)
+            tick("permute")
+        else:
+            moe_route(logits, bias, c.n_group, c.topk_group, c.topk, c.renormalize,
+                      c.routed_scale, topk_ids=b["topk_ids"], topk_w=b["topk_w"], stream=stream)
+            tick("permute")
+            perm = moe_permute(b["topk_ids"], c.E, c.n_shared, c.block_m, workspace=b["perm_ws"],
+                               out=b["perm"], stream=stream)
         n_rows = perm["expert_offsets"][c.E + c.n_shared:]     # device row count
         wf = WFMT[c.wfmt]
         w = self.w

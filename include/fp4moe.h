@@ -127,6 +127,20 @@ int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int n_shared, i
                 int32_t* n_dropped, void* stream);
 
 /*
+ * moe_route_permute -- moe_route followed by moe_permute in one launch, for
+ * decode-sized batches: T*(topk+n_shared) <= 1024.  [GAUDI] "What was built"
+ * (the router) and [NVFP4] "Memory Management" (the dispatch), as for the two
+ * calls; the outputs are bit-identical to moe_route then moe_permute with the
+ * same arguments (no workspace is needed at these sizes).  Larger batches,
+ * and any argument either call rejects, return FP4MOE_ERR_INVALID_ARG.
+ */
+int moe_route_permute(const float* logits, const float* bias, int T, int E, int n_group,
+                      int topk_group, int topk, int renormalize, float routed_scale,
+                      int n_shared, int block_m, int32_t* topk_ids, float* topk_w,
+                      int32_t* expert_offsets, int32_t* sorted_pairs, int32_t* pair_pos,
+                      int32_t* tiles, int32_t* n_tiles, int32_t* n_dropped, void* stream);
+
+/*
  * mxfp4_quant_1x32 -- dynamic 1x32 MXFP4 quantization of bf16 rows.
  * [ATOM] "Stage B: Dynamic Activation Quantization": live bf16 activations
  * become FP4 payloads plus E8M0 scales, one per 32 values along K.

@@ -24,9 +24,10 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
-              "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked"]:
+              "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked",
+              "moe_route_permute"]:
         assert n in names
     for n in names:
         assert getattr(lib, n) is not None
@@ -57,6 +58,19 @@ def test_route_rejects_bad_arguments(bad):
                                                  a["topk_group"], a["topk"], 1, 1.0, None, None,
                                                  None))
     assert st == 1 and "moe_route" in msg
+
+
+def test_route_permute_rejects_large_batches():
+    def run(T, topk=8, ns=1):
+        return _status(lambda lib: lib.moe_route_permute(None, None, T, 384, 8, 4, topk, 1, 1.0, ns,
+                                                         16, None, None, None, None, None, None,
+                                                         None, None, None))
+    st, msg = run(114)                          # 1026 pairs
+    assert st == 1 and "1024" in msg
+    st, msg = run(4, topk=40)
+    assert st == 1 and "topk" in msg
+    st, msg = run(4, ns=9)
+    assert st == 1 and "n_shared" in msg
 
 
 def test_quant_and_convert_reject_bad_K():

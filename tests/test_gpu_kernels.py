@@ -130,6 +130,38 @@ def test_permute_empty(gpu_lib):
     assert np.all(host(out["expert_offsets"]) == 0)
 
 
+# ------------------------------------------------------------------ fused routing + permutation
+
+@pytest.mark.parametrize("T,E,ng,tg,topk,ns,bm,bstd,seed", [
+    (1, 384, 8, 4, 8, 1, 16, 0.1, 21), (8, 384, 8, 4, 8, 1, 16, 0.1, 22),
+    (64, 384, 8, 4, 8, 1, 16, 0.1, 23), (113, 384, 8, 4, 8, 1, 16, 0.1, 24),
+    (16, 8, 1, 1, 2, 0, 16, 0.1, 25), (20, 120, 5, 2, 6, 2, 64, 0.5, 26),
+    (0, 384, 8, 4, 8, 1, 16, 0.1, 27)])
+def test_route_permute_fused(gpu_lib, T, E, ng, tg, topk, ns, bm, bstd, seed):
+    """One launch gives what moe_route then moe_permute give, and the oracle."""
+    g = np.random.default_rng(seed)
+    logits = g.standard_normal((T, E), dtype=np.float32)
+    bias = (g.standard_normal(E, dtype=np.float32) * np.float32(bstd)).astype(np.float32)
+    ids, w, perm = gpu_lib.moe_route_permute(dev(logits), dev(bias), ng, tg, topk, ns, bm)
+    rid, rw = OR.moe_route(logits, bias, ng, tg, topk)
+    assert_equal(host(ids), rid.reshape(T, topk), "topk_ids")
+    np.testing.assert_allclose(host(w), rw.reshape(T, topk), rtol=1e-6, atol=0)
+    ref = OP.moe_permute(rid.reshape(T, topk).astype(np.int32), E, ns, bm)
+    for name in ("expert_offsets", "sorted_pairs", "pair_pos"):
+        assert_equal(host(perm[name]), ref[name], name)
+    nt = int(host(perm["n_tiles"])[0])
+    assert nt == ref["n_tiles"]
+    assert_equal(host(perm["tiles"])[:nt], ref["tiles"], "tiles")
+    assert int(host(perm["n_dropped"])[0]) == ref["n_dropped"]
+    if T:
+        # and bit for bit what the two separate calls write
+        ids2, w2 = gpu_lib.moe_route(dev(logits), dev(bias), ng, tg, topk)
+        perm2 = gpu_lib.moe_permute(ids2, E, ns, bm)
+        assert_equal(host(w), host(w2), "weights vs moe_route")
+        for name in ("expert_offsets", "sorted_pairs", "pair_pos"):
+            assert_equal(host(perm[name]), host(perm2[name]), name + " vs moe_permute")
+
+
 # ------------------------------------------------------------------ MXFP4 quant
 
 def _quant_inputs(seed, M, K):
