@@ -46,6 +46,7 @@ class GemmArgs(ctypes.Structure):
         ("tiles", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_f32", ctypes.c_void_p),
         ("w_layout", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_int),
+        ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p), ("out_q_rows", ctypes.c_int),
     ]
 
 
@@ -247,12 +248,15 @@ def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=N
 def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale=None,
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
                      gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
-                     a_layout=0, stream=None):
+                     a_layout=0, out_q=None, out_q_scale=None, no_out=False, stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
     codes [rows, K/2] with a_scale [rows, K/32] (a_layout 0), or chunk-major
     MXFP4 codes [K/128, rows, 64] with a_scale [K/128, rows, 4] (a_layout 1).
+    out_q / out_q_scale (stage 1, block_m 192): chunk-major MXFP4 copies of the
+    output [N_out/128, rows, 64] / [N_out/128, rows, 4]; with no_out=True the
+    bf16 output is not written (returns None).
     Returns out bf16 [max_rows, N_out]."""
     lib = load()
     E, N = w.shape[0], w.shape[1]
@@ -271,7 +275,7 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
     else:
         a_ = a
         lda = a.stride(0) * 2
-    if out is None:
+    if out is None and not no_out:
         out = torch.empty((max_rows, n_out), dtype=torch.bfloat16, device=_dev(a))
     args = GemmArgs(stage, wfmt, afmt, E, N, K, max_rows, perm["max_tiles"], block_m, gather_div,
                     w.data_ptr(), None if w_scale is None else w_scale.data_ptr(),
@@ -280,8 +284,12 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     a_.data_ptr(), None if a_scale is None else a_scale.data_ptr(), lda,
                     None if a_row_gather is None else a_row_gather.data_ptr(),
                     perm["expert_offsets"].data_ptr(), perm["tiles"].data_ptr(),
-                    perm["n_tiles"].data_ptr(), out.data_ptr(), out.stride(0),
-                    None if out_f32 is None else out_f32.data_ptr(), w_layout, a_layout, a_rows)
+                    perm["n_tiles"].data_ptr(), None if out is None else out.data_ptr(),
+                    n_out if out is None else out.stride(0),
+                    None if out_f32 is None else out_f32.data_ptr(), w_layout, a_layout, a_rows,
+                    None if out_q is None else out_q.data_ptr(),
+                    None if out_q_scale is None else out_q_scale.data_ptr(),
+                    0 if out_q is None else out_q.shape[1])
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
 

@@ -101,8 +101,19 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: block_m 192 needs ldo %% 8 == 0 and a 16-byte aligned out");
   FP4MOE_REQUIRE(a_chunked || (a->lda >= a->K && a->lda % 32 == 0), "fp4_grouped_gemm: lda=%lld",
                  (long long)a->lda);
+  const bool quant_out = a->out_q != nullptr || a->out_q_scale != nullptr;
+  FP4MOE_REQUIRE(!quant_out || (a->out_q && a->out_q_scale && a->stage == 1 && a->block_m == 192 &&
+                                a->afmt == FP4MOE_A_MXFP4 && !a->out_f32 &&
+                                (a->N / 2) % 128 == 0),
+                 "fp4_grouped_gemm: out_q needs both buffers, stage 1, block_m 192, MXFP4 "
+                 "activations, no out_f32 and an output width that is a multiple of 128");
+  FP4MOE_REQUIRE(!quant_out || (a->out_q_rows >= a->max_rows && a->out_q_rows <= (1 << 26)),
+                 "fp4_grouped_gemm: out_q_rows=%d (max_rows=%d)", a->out_q_rows, a->max_rows);
+  FP4MOE_REQUIRE(!quant_out || ((uintptr_t)a->out_q & 3) == 0,
+                 "fp4_grouped_gemm: out_q must be 4-byte aligned");
   if (a->max_tiles == 0 || a->max_rows == 0) return FP4MOE_OK;
-  FP4MOE_REQUIRE(a->w && a->a && a->expert_offsets && a->tiles && a->n_tiles && a->out,
+  FP4MOE_REQUIRE(a->w && a->a && a->expert_offsets && a->tiles && a->n_tiles &&
+                     (a->out || quant_out),
                  "fp4_grouped_gemm: null pointer");
   FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_FP8 || a->w_scale, "fp4_grouped_gemm: w_scale is null");
   FP4MOE_REQUIRE(a->wfmt != FP4MOE_W_NVFP4 || a->w_tensor_scale,
@@ -138,6 +149,9 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.n_tiles = a->n_tiles;
   p.out = a->out;
   p.out_f32 = a->out_f32;
+  p.q_codes = a->out_q;
+  p.q_scales = a->out_q_scale;
+  p.q_rows = a->out_q_rows;
   hipStream_t s = as_stream(stream);
   const int mt = a->max_tiles;
   const int st = a->stage;

@@ -62,6 +62,9 @@ struct GemmParams {
   const int32_t* n_tiles;
   uint16_t* out;
   float* out_f32;
+  uint8_t* q_codes;          // stage-1 output quantized (chunk-major), or NULL
+  uint8_t* q_scales;
+  int q_rows;
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

@@ -984,7 +984,26 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
             const int row = q * RPI + lane / LPR;
             const uint4 v = *reinterpret_cast<const uint4*>(ep + row * EP_PITCH + (lane % LPR) * 16);
             const int r = wrow0 + i3 * 32 + hh * 16 + row;
-            if (r < row_end) *reinterpret_cast<uint4*>(p.out + (int64_t)r * p.ldo + out_col) = v;
+            if (p.out && r < row_end) *reinterpret_cast<uint4*>(p.out + (int64_t)r * p.ldo + out_col) = v;
+            if (STAGE == 1 && p.q_codes) {
+              // MXFP4 of the bf16 row piece, as mxfp4_quant_1x32 computes it: a
+              // 32-column block is 4 adjacent lanes (8 values each)
+              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+              uint32_t amax = 0;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+              amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, false));
+              amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, false));
+              const uint32_t sbyte = (uint32_t)max((int)(amax >> 7) - 2, 0);
+              const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^-e
+              const uint32_t packed = e2m1_pack8(w, inv, amax > 0x7f80u);
+              if (r < row_end) {
+                const int64_t k = out_col;                  // h column of the lane's first value
+                const int64_t slab = (k >> 7) * p.q_rows + r;
+                *reinterpret_cast<uint32_t*>(p.q_codes + slab * 64 + ((k & 127) >> 1)) = packed;
+                if ((lane & 3) == 0) p.q_scales[slab * 4 + ((k & 127) >> 5)] = (uint8_t)sbyte;
+              }
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
         }

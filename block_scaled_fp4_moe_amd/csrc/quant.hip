@@ -17,15 +17,6 @@
 
 namespace fp4moe {
 
-// E2M1 code magnitude (0..7) of |q| by round-to-nearest-even on the grid
-// {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6: ties 0.25, 1.25, 2.5, 5 go
-// down and 0.75, 1.75, 3.5 go up, always to the even code.
-__device__ __forceinline__ uint32_t e2m1_mag_code(float a) {
-  return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-         (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-         (uint32_t)(a > 5.0f);
-}
-
 __device__ __forceinline__ float e2m1_mag_value(uint32_t c) {
   // codes 0..7 -> 0, .5, 1, 1.5, 2, 3, 4, 6
   return c < 4 ? 0.5f * (float)c : (c == 7 ? 6.0f : (float)(c - 2));
@@ -107,18 +98,10 @@ __global__ __launch_bounds__(256) void mxfp4_quant_kernel(
     const int f = (int)(amax >> 7);                 // bf16 biased exponent of amax
     const uint32_t sbyte = (uint32_t)max(f - 2, 0);
     const float inv = __uint_as_float((254u - sbyte) << 23);   // 2^(127 - sbyte) = 2^-e
+    const bool has_nan = amax > 0x7f80u;
     uint32_t packed[4];
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t h = (w[4 * d + (i >> 1)] >> (16 * (i & 1))) & 0xffffu;
-        const float q = bf16_to_f32(h & 0x7fffu) * inv;
-        word |= (e2m1_mag_code(q) | ((h >> 12) & 8u)) << (4 * i);
-      }
-      packed[d] = word;
-    }
+    for (int d = 0; d < 4; ++d) packed[d] = e2m1_pack8(w + 4 * d, inv, has_nan);
     const uint4 cv = make_uint4(packed[0], packed[1], packed[2], packed[3]);
     if (CHUNKED) {
       const int n_dst = row_map ? map_k : 1;

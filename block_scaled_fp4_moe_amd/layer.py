@@ -4,7 +4,8 @@ Order ([ATOM] "Stage D: MXFP4 Fused MoE", [NVFP4] "Weight Dequantization and
 Activation QDQ"): moe_route -> moe_permute (one launch, moe_route_permute, at
 decode sizes) -> activation quantization
 (mxfp4_quant_1x32 | nvfp4_qdq | none) -> fp4_grouped_gemm stage 1 (gate/up,
-SiLU*up) -> quantization of h -> fp4_grouped_gemm stage 2 (down) ->
+SiLU*up) -> quantization of h (in the stage-1 epilogue for 192-row tiles) ->
+fp4_grouped_gemm stage 2 (down) ->
 moe_combine.  Every step is a kernel of libfp4moe; this module only
 allocates device buffers (once per token count) and passes pointers.
 """
@@ -165,12 +166,18 @@ class MoELayer:
         ts13 = w.get("w13_ts") if c.wfmt == "nvfp4" else None
         cs13 = w["w13_scale"] if c.wfmt == "fp8" else None
         tick("stage1")
+        # 192-row tiles quantize h for stage 2 in their epilogue (the bf16 h is
+        # then written only when the caller keeps the intermediates)
+        fused_q = self.chunked and c.block_m == 192
+        qkw = dict(out_q=b["hq"], out_q_scale=b["hs"], no_out=not keep) if fused_q else {}
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
-                         out=b["h"], w_layout=self.layout, a_layout=a_layout, stream=stream,
-                         **gather)
+                         out=b["h"] if (keep or not fused_q) else None, w_layout=self.layout,
+                         a_layout=a_layout, stream=stream, **qkw, **gather)
         tick("quant2")
-        if c.afmt == "mx" and self.chunked:
+        if fused_q:
+            a2, a2s = b["hq"], b["hs"]
+        elif c.afmt == "mx" and self.chunked:
             mxfp4_quant_1x32_chunked(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
                                      stream=stream)
             a2, a2s = b["hq"], b["hs"]

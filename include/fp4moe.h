@@ -218,6 +218,12 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * layout of mxfp4_quant_1x32_chunked; lda unused) is taken by (MXFP4,
  * MXFP4) with fragment-major weights and block_m 128, 192 or 256; other
  * combinations return FP4MOE_ERR_INVALID_ARG.
+ * out_q / out_q_scale (stage 1, block_m 192, MXFP4 activations, out_f32 NULL):
+ * the stage-1 output h is also written quantized exactly as
+ * mxfp4_quant_1x32_chunked(bf16 h, out_rows = out_q_rows) writes it -- the
+ * stage-2 activations of [ATOM] "Stage B" without a separate pass over h;
+ * out may then be NULL (h not written in bf16).  Rows past a segment's end
+ * are not written.
  */
 typedef struct {
   int stage;               /* 1 or 2                                                */
@@ -247,6 +253,9 @@ typedef struct {
   int w_layout;            /* FP4MOE_LAYOUT_* of w and w_scale                      */
   int a_layout;            /* FP4MOE_A_LAYOUT_* of a and a_scale (MXFP4 only)       */
   int a_rows;              /* chunked layout: rows per K chunk slab of a / a_scale  */
+  uint8_t* out_q;          /* optional: stage-1 output as MXFP4 codes, chunked      */
+  uint8_t* out_q_scale;    /*   and its E8M0 scales (see below)                     */
+  int out_q_rows;          /*   rows per K chunk slab of out_q / out_q_scale        */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);

@@ -105,8 +105,9 @@ def test_gemm_rejects_unsupported_combinations():
         args = fm.GemmArgs(a["stage"], a["wfmt"], a["afmt"], a["n_experts"], a["N"], a["K"],
                            a["max_rows"], a["max_tiles"], a["block_m"], a["gather_div"],
                            None, None, None, None, None, None, a["lda"], None, None, None, None,
-                           None, a["ldo"], None, a.get("w_layout", 0), a.get("a_layout", 0),
-                           a.get("a_rows", 0))
+                           None, a["ldo"], a.get("out_f32"), a.get("w_layout", 0),
+                           a.get("a_layout", 0), a.get("a_rows", 0), a.get("out_q"),
+                           a.get("out_q_scale"), a.get("out_q_rows", 0))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -145,6 +146,16 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**{**wide8, "N": 320}, max_tiles=0)[0] == 1       # output width 160
     assert run(**{**wide8, "N": 128}, stage=2, max_tiles=0)[0] == 1
     assert run(**{**wide8, "afmt": 0}, max_tiles=0)[0] == 1      # bf16 activations: 16/32/64
+    # stage-1 output quantized in the epilogue: block_m 192, MXFP4 activations,
+    # both buffers, no fp32 copy, enough rows (pointers are never touched here)
+    q = dict(out_q=64, out_q_scale=128, out_q_rows=8, max_tiles=0)
+    assert run(**wide, **q)[0] == 0
+    assert run(**wide8, **q)[0] == 0
+    assert run(**wide, **{**q, "out_q_scale": None})[0] == 1
+    assert run(**wide, **q, stage=2)[0] == 1
+    assert run(**{**wide, "block_m": 256, "ldo": 256}, **q)[0] == 1
+    assert run(**wide, **{**q, "out_q_rows": 4})[0] == 1       # < max_rows
+    assert run(**wide, **q, out_f32=256)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 
 

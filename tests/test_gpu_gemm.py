@@ -65,7 +65,7 @@ def routing(rng, T, topk, E, skew=False):
 
 
 def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
-              exact=False, layout=0, a_layout=0, with_f32=True):
+              exact=False, layout=0, a_layout=0, with_f32=True, quant_out=False):
     rng = np.random.default_rng(seed)
     Et = E + ns
     k = topk + ns
@@ -129,9 +129,34 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
         wkw["w"] = c
         if wfmt != "fp8":
             wkw["w_scale"] = sc
+    qkw = {}
+    if quant_out:
+        # stage-1 output also quantized in the epilogue; unwritten bytes stay 0xEE
+        rows = T * k
+        qkw = dict(out_q=torch.full((n_out // 128, rows, 64), 0xEE, dtype=torch.uint8, device="cuda"),
+                   out_q_scale=torch.full((n_out // 128, rows, 4), 0xEE, dtype=torch.uint8,
+                                          device="cuda"))
     out = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.WFMT[wfmt], afmt_code,
                                    perm=perm, block_m=bm, out_f32=out_f32, w_layout=layout,
-                                   a_layout=a_layout, **wkw, **a_kw, **gather)
+                                   a_layout=a_layout, **wkw, **a_kw, **gather, **qkw)
+    if quant_out:
+        # the codes are mxfp4_quant_1x32 of the bf16 output rows, in the
+        # chunk-major layout; rows past the valid count are not written
+        h_bits = bits_of(out)[:n_rows]
+        rc, rs = OQ.mxfp4_quant_1x32(h_bits)
+        cc, cs = chunk_major(rc, rs)
+        gq, gs = host(qkw["out_q"]), host(qkw["out_q_scale"])
+        assert np.array_equal(gq[:, :n_rows], cc), "quantized h codes"
+        assert np.array_equal(gs[:, :n_rows], cs), "quantized h scales"
+        assert np.all(gq[:, n_rows:] == 0xEE) and np.all(gs[:, n_rows:] == 0xEE), "rows past the end"
+        # and the same bytes when the bf16 output is not written at all
+        q2 = dict(out_q=torch.zeros_like(qkw["out_q"]), out_q_scale=torch.zeros_like(qkw["out_q_scale"]))
+        none = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.WFMT[wfmt], afmt_code, perm=perm, block_m=bm,
+                                        w_layout=layout, a_layout=a_layout, no_out=True, **wkw,
+                                        **a_kw, **gather, **q2)
+        assert none is None
+        assert np.array_equal(host(q2["out_q"])[:, :n_rows], cc), "quantized h codes, no bf16 out"
+        assert np.array_equal(host(q2["out_q_scale"])[:, :n_rows], cs), "scales, no bf16 out"
     ref_unrounded = OG.grouped_stage(stage, a_sorted, perm_ref["expert_offsets"],
                                      lambda e: oracle_weight(wd, wfmt, e), rounding=False)
     g_bits = bits_of(out)[:n_rows]
@@ -229,6 +254,16 @@ def test_mx_gemm_wide_tiles_bf16_only(gpu_lib, case, a_layout):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
     run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
               layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=a_layout, with_f32=False)
+
+
+@pytest.mark.parametrize("a_layout", [0, 1])
+@pytest.mark.parametrize("case", [c for c in WIDE_CASES if c[0] == 1])
+def test_wide_stage1_quantized_output(gpu_lib, case, a_layout):
+    """Stage 1 on 192-row tiles writes h also as chunk-major MXFP4, exactly
+    what mxfp4_quant_1x32 makes of the bf16 h."""
+    stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
+    run_stage(gpu_lib, stage, wfmt, "mx", T, topk, E, ns, H, I, bm, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=a_layout, with_f32=False, quant_out=True)
 
 
 @pytest.mark.parametrize("case", [c for c in MX_CASES if c[1] == "mx" and c[8] >= 128] + WIDE_CASES)
