@@ -228,6 +228,12 @@ WIDE_CASES = [
     (2, "fp8", 400, 4, 8, 1, 512, 256, 192, 44, True),
     (1, "fp8", 300, 8, 8, 1, 1024, 128, 192, 45, False),
     (2, "fp8", 100, 2, 4, 0, 256, 128, 192, 46, False),
+    # more work items than workgroups (several items per workgroup, the FP8
+    # tile prefetching the next item's first chunks), K of two chunks
+    (1, "fp8", 1500, 8, 8, 1, 256, 512, 192, 47, True),
+    (2, "fp8", 1500, 8, 8, 1, 1024, 256, 192, 48, True),
+    (1, "mx", 1500, 8, 8, 1, 256, 1024, 192, 49, True),
+    (2, "mx", 1500, 8, 8, 1, 2048, 256, 192, 50, True),
 ]
 
 

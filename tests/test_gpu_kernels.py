@@ -210,6 +210,22 @@ def chunk_major(codes, scales):
             np.ascontiguousarray(scales.reshape(M, kb // 64, 4).transpose(1, 0, 2)))
 
 
+def test_mxfp4_quant_every_finite_bf16(gpu_lib):
+    """Every finite bf16 pattern goes through the quantizer (the E2M1 codes come
+    from the hardware conversion): sorted by magnitude, so that each block holds
+    neighbouring values and the codes span the grid, and in a seeded shuffle."""
+    pats = np.arange(65536, dtype=np.uint32)
+    finite = pats[(pats & 0x7F80) != 0x7F80].astype(np.uint16)
+    n = (finite.size // 256) * 256
+    order = np.argsort(finite & 0x7FFF, kind="stable")
+    for xb in (finite[order][:n], np.random.default_rng(5).permutation(finite)[:n]):
+        xb = xb.reshape(-1, 256)
+        codes, scales = gpu_lib.mxfp4_quant_1x32(bf16_dev(xb))
+        rc, rs = OQ.mxfp4_quant_1x32(xb)
+        assert_equal(host(scales), rs, "scales")
+        assert_equal(host(codes), rc, "codes")
+
+
 @pytest.mark.parametrize("M,K", [(8, 128), (37, 512), (64, 7168)])
 def test_mxfp4_quant_chunked_parity(gpu_lib, M, K):
     xb = _quant_inputs(M * 3 + K, M, K)
