@@ -10,8 +10,10 @@
 // rank is the popcount of lower peer lanes, and the lowest peer advances the
 // expert's running position in LDS.
 //
-// Small batches (T*k <= kSmallPairs) run everything in one wavefront: one
-// launch.  Larger batches use three kernels: per-chunk histograms, one
+// Small batches (T*k <= kSmallPairs) take one launch: with at most
+// kHistMaxExperts experts, one wavefront per 64 pairs and per-group
+// histograms (permute_hist_body); with more experts, one wavefront that
+// visits the groups in order.  Larger batches use three kernels: per-chunk histograms, one
 // block that scans them (and writes offsets and tiles), and per-chunk scatters.
 #include "permute_dev.h"
 
@@ -27,6 +29,16 @@ __global__ __launch_bounds__(64) void permute_small_kernel(
   __shared__ PermuteSmallScratch scratch;
   permute_small_body(ids, T, topk, E, n_shared, block_m, expert_offsets, sorted_pairs, pair_pos,
                      tiles, n_tiles, n_dropped, scratch);
+}
+
+__global__ __launch_bounds__(1024) void permute_small_hist_kernel(
+    const int32_t* __restrict__ ids, int T, int topk, int E, int n_shared, int block_m,
+    int max_tiles, int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_pairs,
+    int32_t* __restrict__ pair_pos, int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles,
+    int32_t* __restrict__ n_dropped) {
+  __shared__ PermuteHistScratch scratch;
+  permute_hist_body(ids, T, topk, E, n_shared, block_m, max_tiles, expert_offsets, sorted_pairs,
+                    pair_pos, tiles, n_tiles, n_dropped, scratch);
 }
 
 // ---- large path ------------------------------------------------------------
@@ -129,6 +141,13 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int 
   FP4MOE_REQUIRE(T == 0 || (topk_ids && sorted_pairs && pair_pos), "moe_permute: null pointer");
   FP4MOE_CHECK_DEVICE();
   hipStream_t s = as_stream(stream);
+  if (P <= kSmallPairs && E + n_shared <= kHistMaxExperts) {
+    const int nw = P > 64 ? (int)((P + 63) / 64) : 1;
+    hipLaunchKernelGGL(permute_small_hist_kernel, dim3(1), dim3(64 * nw), 0, s, topk_ids, T, topk,
+                       E, n_shared, block_m, moe_permute_max_tiles(T, topk, E, n_shared, block_m),
+                       expert_offsets, sorted_pairs, pair_pos, tiles, n_tiles, n_dropped);
+    return check_launch("moe_permute");
+  }
   if (P <= kSmallPairs) {
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(64), 0, s, topk_ids, T, topk, E,
                        n_shared, block_m, expert_offsets, sorted_pairs, pair_pos, tiles, n_tiles,

@@ -16,6 +16,7 @@
 
 namespace fp4moe {
 
+template <int PM>
 __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias, int E,
                                                    int n_group, int topk_group, int topk,
@@ -23,7 +24,7 @@ __global__ __launch_bounds__(64) void route_kernel(const float* __restrict__ log
                                                    int32_t* __restrict__ topk_ids,
                                                    float* __restrict__ topk_w) {
   __shared__ RouteScratch scratch;
-  route_token(logits, bias, E, n_group, topk_group, topk, renormalize, routed_scale, blockIdx.x,
+  route_token<PM>(logits, bias, E, n_group, topk_group, topk, renormalize, routed_scale, blockIdx.x,
               topk_ids, topk_w, scratch, nullptr);
 }
 
@@ -46,7 +47,10 @@ extern "C" int moe_route(const float* logits, const float* bias, int T, int E, i
   if (T == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(logits && topk_ids && topk_w, "moe_route: null pointer");
   FP4MOE_CHECK_DEVICE();
-  hipLaunchKernelGGL(route_kernel, dim3(T), dim3(64), 0, as_stream(stream), logits, bias, E,
-                     n_group, topk_group, topk, renormalize, routed_scale, topk_ids, topk_w);
+#define FP4MOE_ROUTE_LAUNCH(PM)                                                                 \
+  hipLaunchKernelGGL(route_kernel<PM>, dim3(T), dim3(64), 0, as_stream(stream), logits, bias, E, \
+                     n_group, topk_group, topk, renormalize, routed_scale, topk_ids, topk_w)
+  FP4MOE_ROUTE_PM_SWITCH(E, FP4MOE_ROUTE_LAUNCH)
+#undef FP4MOE_ROUTE_LAUNCH
   return check_launch("moe_route");
 }

@@ -21,10 +21,11 @@ from . import (A_BF16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAG
                mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
 
 
-# moe_route_permute (one launch) takes T * (topk + n_shared) up to 1024 pairs; it
-# measured faster than the two launches only for the smallest batches, where
-# the permutation is one wavefront group.
-ROUTE_PERMUTE_MAX_PAIRS = 64
+# moe_route_permute (one launch, one workgroup) takes T * (topk + n_shared) up
+# to 1024 pairs.  It routes one token per wavefront of a single CU, so beyond
+# about 8 tokens the two launches (one workgroup per token for the routing)
+# measured faster.
+ROUTE_PERMUTE_MAX_TOKENS = 8
 
 
 @dataclass
@@ -131,7 +132,7 @@ class MoELayer:
         k = c.topk + c.n_shared
         b = self._buffers(T)
         tick("route")
-        if T * k <= ROUTE_PERMUTE_MAX_PAIRS:
+        if T <= ROUTE_PERMUTE_MAX_TOKENS and T * k <= 1024:
             # decode sizes: routing and permutation in one launch
             _, _, perm = moe_route_permute(logits, bias, c.n_group, c.topk_group, c.topk,
                                            c.n_shared, c.block_m, c.renormalize, c.routed_scale,

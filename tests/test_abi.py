@@ -38,7 +38,7 @@ def test_permute_size_queries_match_oracle_bound():
     for T, topk, E, ns, bm in [(1, 8, 384, 1, 16), (64, 8, 384, 1, 16), (8192, 8, 384, 1, 256),
                                (16, 2, 8, 0, 16), (0, 8, 384, 1, 16), (5, 1, 8, 0, 4)]:
         assert lib.moe_permute_max_tiles(T, topk, E, ns, bm) == OP.max_tiles(T, topk, E, ns, bm)
-    assert lib.moe_permute_workspace(64, 8, 384, 1, 16) == 0          # single-wave path
+    assert lib.moe_permute_workspace(64, 8, 384, 1, 16) == 0          # single-launch path
     assert lib.moe_permute_workspace(8192, 8, 384, 1, 256) == 72 * 385 * 4
 
 

@@ -49,6 +49,11 @@ ROUTE_CASES = [
     (777, 384, 8, 4, 8, 0.1, 3),
     (33, 256, 8, 4, 8, 0.0, 4),
     (5, 1024, 16, 2, 32, 0.5, 5),
+    # group layouts: lanes per group 16 and 32, one expert per lane, an
+    # experts-per-lane bound above ceil(E/64), groups that are not lane runs
+    (40, 384, 4, 2, 8, 0.1, 6), (40, 384, 2, 1, 8, 0.1, 7), (20, 64, 2, 1, 4, 0.2, 8),
+    (20, 128, 4, 2, 6, 0.1, 9), (12, 512, 8, 3, 10, 0.1, 10), (9, 320, 8, 4, 8, 0.1, 11),
+    (7, 600, 6, 3, 8, 0.1, 12),
 ]
 
 
@@ -105,7 +110,8 @@ def _perm_check(gpu_lib, ids, E, n_shared, bm):
 
 @pytest.mark.parametrize("T,topk,E,ns,bm,seed", [
     (1, 8, 384, 1, 16, 1), (8, 8, 384, 1, 16, 2), (64, 8, 384, 1, 16, 3),
-    (113, 8, 384, 1, 16, 4),            # 1017 pairs: single-wave path
+    (113, 8, 384, 1, 16, 4),            # 1017 pairs: single-launch path
+    (20, 8, 2000, 1, 16, 10),           # more experts than the histogram form holds
     (114, 8, 384, 1, 16, 5),            # 1026 pairs: three-kernel path
     (3000, 8, 384, 1, 64, 6), (2048, 8, 384, 0, 256, 7), (16, 2, 8, 0, 16, 8),
     (500, 4, 4000, 2, 32, 9)])
@@ -136,7 +142,10 @@ def test_permute_empty(gpu_lib):
     (1, 384, 8, 4, 8, 1, 16, 0.1, 21), (8, 384, 8, 4, 8, 1, 16, 0.1, 22),
     (64, 384, 8, 4, 8, 1, 16, 0.1, 23), (113, 384, 8, 4, 8, 1, 16, 0.1, 24),
     (16, 8, 1, 1, 2, 0, 16, 0.1, 25), (20, 120, 5, 2, 6, 2, 64, 0.5, 26),
-    (0, 384, 8, 4, 8, 1, 16, 0.1, 27)])
+    (0, 384, 8, 4, 8, 1, 16, 0.1, 27),
+    (100, 1024, 16, 2, 8, 1, 16, 0.5, 28),   # 900 pairs over 8 wavefronts (E > 512)
+    (40, 384, 2, 1, 8, 1, 32, 0.1, 29), (70, 384, 4, 2, 8, 0, 64, 0.0, 30),
+    (9, 320, 8, 4, 8, 3, 1, 0.1, 31)])
 def test_route_permute_fused(gpu_lib, T, E, ng, tg, topk, ns, bm, bstd, seed):
     """One launch gives what moe_route then moe_permute give, and the oracle."""
     g = np.random.default_rng(seed)
@@ -160,6 +169,25 @@ def test_route_permute_fused(gpu_lib, T, E, ng, tg, topk, ns, bm, bstd, seed):
         assert_equal(host(w), host(w2), "weights vs moe_route")
         for name in ("expert_offsets", "sorted_pairs", "pair_pos"):
             assert_equal(host(perm[name]), host(perm2[name]), name + " vs moe_permute")
+
+
+def test_route_permute_fused_ties(gpu_lib):
+    """Coarse logits: many equal keys inside and across groups, several tokens
+    per wavefront."""
+    g = np.random.default_rng(32)
+    T, E = 100, 384
+    logits = (np.round(g.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    bias = np.zeros(E, dtype=np.float32)
+    ids, w, perm = gpu_lib.moe_route_permute(dev(logits), dev(bias), 8, 4, 8, 1, 16)
+    rid, rw = OR.moe_route(logits, bias, 8, 4, 8)
+    assert_equal(host(ids), rid.reshape(T, 8), "topk_ids")
+    np.testing.assert_allclose(host(w), rw.reshape(T, 8), rtol=1e-6, atol=0)
+    ref = OP.moe_permute(rid.reshape(T, 8).astype(np.int32), E, 1, 16)
+    for name in ("expert_offsets", "sorted_pairs", "pair_pos"):
+        assert_equal(host(perm[name]), ref[name], name)
+    nt = int(host(perm["n_tiles"])[0])
+    assert nt == ref["n_tiles"]
+    assert_equal(host(perm["tiles"])[:nt], ref["tiles"], "tiles")
 
 
 # ------------------------------------------------------------------ MXFP4 quant
