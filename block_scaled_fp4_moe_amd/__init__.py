@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp4moe.so")
 
 W_MXFP4, W_NVFP4, W_FP8 = 0, 1, 2
-A_BF16, A_MXFP4 = 0, 1
+A_BF16, A_MXFP4, A_F16 = 0, 1, 2
 LAYOUT_ROWMAJOR, LAYOUT_FRAGMENT = 0, 1
 A_LAYOUT_ROWMAJOR, A_LAYOUT_CHUNKED = 0, 1
 WFMT = {"mx": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8}
@@ -47,6 +47,7 @@ class GemmArgs(ctypes.Structure):
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_f32", ctypes.c_void_p),
         ("w_layout", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_int),
         ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p), ("out_q_rows", ctypes.c_int),
+        ("a_f16_scale", ctypes.c_void_p),
     ]
 
 
@@ -70,7 +71,7 @@ def load():
         "mxfp4_quant_1x32": ([P, I, I, I64, P, P, P, P, P], I),
         "mxfp4_quant_1x32_chunked": ([P, I, I, I64, P, I, I, P, P, P, P], I),
         "nvfp4_qdq_workspace": ([], S),
-        "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, S, P], I),
+        "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, P, P, S, P], I),
         "fp4_grouped_gemm": ([ctypes.POINTER(GemmArgs), P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P, P], I),
         "fp4_weight_preshuffle": ([I, I, I, I, P, P, P, P, P], I),
@@ -103,8 +104,8 @@ def _dev(t):
 
 
 def _u16(x):
-    """bf16 tensor (or its int16/uint16 bit view) -> int16 view for pointer passing."""
-    if x.dtype == torch.bfloat16:
+    """bf16 / f16 tensor (or its int16/uint16 bit view) -> int16 view for pointer passing."""
+    if x.dtype in (torch.bfloat16, torch.float16):
         return x.view(torch.int16)
     assert x.dtype in (torch.int16, torch.uint16), x.dtype
     return x
@@ -230,17 +231,22 @@ def mxfp4_quant_1x32_chunked(x, row_map=None, map_k=1, out_rows=None, row_count=
 
 
 def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=None,
-              tensor_scale_out=None, workspace=None, stream=None):
-    """x bf16 [M, K] -> y bf16 [M, K] (and optional codes, scales, tensor scale)."""
+              tensor_scale_out=None, y_f16=None, y_f16_scale=None, no_y=False, workspace=None,
+              stream=None):
+    """x bf16 [M, K] -> y bf16 [M, K] (and optional codes, scales, tensor scale, and
+    the f16 operand form y_f16 [M, K] float16 with its factor y_f16_scale [1]).
+    With no_y=True (y_f16 given) y is not written and None is returned."""
     lib = load()
     xs = _u16(x).contiguous()
     M, K = xs.shape
-    if y is None:
+    if y is None and not no_y:
         y = torch.empty((M, K), dtype=torch.bfloat16, device=_dev(x))
     if workspace is None and tensor_scale is None:
         workspace = torch.empty(lib.nvfp4_qdq_workspace(), dtype=torch.uint8, device=_dev(x))
-    _check(lib.nvfp4_qdq(_p(xs), M, K, _p(row_count), _p(tensor_scale), _p(_u16(y)), _p(codes),
-                         _p(scales), _p(tensor_scale_out), _p(workspace),
+    _check(lib.nvfp4_qdq(_p(xs), M, K, _p(row_count), _p(tensor_scale),
+                         None if y is None else _p(_u16(y)), _p(codes), _p(scales),
+                         _p(tensor_scale_out), None if y_f16 is None else _p(_u16(y_f16)),
+                         _p(y_f16_scale), _p(workspace),
                          0 if workspace is None else workspace.numel(), _stream(stream)))
     return y
 
@@ -248,12 +254,15 @@ def nvfp4_qdq(x, tensor_scale=None, row_count=None, y=None, codes=None, scales=N
 def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale=None,
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
                      gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
-                     a_layout=0, out_q=None, out_q_scale=None, no_out=False, stream=None):
+                     a_layout=0, out_q=None, out_q_scale=None, no_out=False, a_f16_scale=None,
+                     stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
     codes [rows, K/2] with a_scale [rows, K/32] (a_layout 0), or chunk-major
     MXFP4 codes [K/128, rows, 64] with a_scale [K/128, rows, 4] (a_layout 1).
+    afmt A_F16: a is the f16 operand form of nvfp4_qdq (viewed as int16 / float16)
+    and a_f16_scale its float32 [1] power-of-two factor.
     out_q / out_q_scale (stage 1, block_m 192): chunk-major MXFP4 copies of the
     output [N_out/128, rows, 64] / [N_out/128, rows, 4]; with no_out=True the
     bf16 output is not written (returns None).
@@ -265,7 +274,7 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
     if max_rows is None:
         max_rows = perm["sorted_pairs"].shape[0]
     a_rows = 0
-    if afmt == A_BF16:
+    if afmt in (A_BF16, A_F16):
         a_ = _u16(a)
         lda = a_.stride(0)
     elif a_layout == A_LAYOUT_CHUNKED:
@@ -289,7 +298,8 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     None if out_f32 is None else out_f32.data_ptr(), w_layout, a_layout, a_rows,
                     None if out_q is None else out_q.data_ptr(),
                     None if out_q_scale is None else out_q_scale.data_ptr(),
-                    0 if out_q is None else out_q.shape[1])
+                    0 if out_q is None else out_q.shape[1],
+                    None if a_f16_scale is None else a_f16_scale.data_ptr())
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
 

@@ -35,12 +35,23 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   // FP8 weights x MXFP4 activations on the scaled MFMA: 192-row tiles
   const bool mx8 = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_FP8 && a->block_m == 192;
   const bool dq = !mx && !mx8;
-  FP4MOE_REQUIRE(a->afmt == FP4MOE_A_BF16 || a->afmt == FP4MOE_A_MXFP4,
+  FP4MOE_REQUIRE(a->afmt == FP4MOE_A_BF16 || a->afmt == FP4MOE_A_MXFP4 ||
+                     a->afmt == FP4MOE_A_F16,
                  "fp4_grouped_gemm: afmt=%d", a->afmt);
   FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4 || a->wfmt == FP4MOE_W_FP8,
                  "fp4_grouped_gemm: wfmt=%d", a->wfmt);
   FP4MOE_REQUIRE(!(a->wfmt == FP4MOE_W_NVFP4 && a->afmt == FP4MOE_A_MXFP4),
                  "fp4_grouped_gemm: NVFP4 weights take bf16 activations (nvfp4_qdq output)");
+  // f16 activations: the NVFP4 tiled path only (E2M1 x E4M3 is exact in f16)
+  const bool f16a = a->afmt == FP4MOE_A_F16;
+  FP4MOE_REQUIRE(!f16a || (a->wfmt == FP4MOE_W_NVFP4 && a->block_m == 64 &&
+                           a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
+                           a->a_layout == FP4MOE_A_LAYOUT_ROWMAJOR),
+                 "fp4_grouped_gemm: f16 activations need NVFP4 fragment-major weights, block_m "
+                 "64 and row-major A");
+  FP4MOE_REQUIRE(!f16a || (a->stage == 1 ? a->N / 2 : a->N) % (a->stage == 1 ? 128 : 256) == 0,
+                 "fp4_grouped_gemm: f16 activations need an output width that is a multiple "
+                 "of 128 (stage 1) or 256 (stage 2)");
   FP4MOE_REQUIRE(a->K > 0 && a->K % 128 == 0, "fp4_grouped_gemm: K=%d not a multiple of 128", a->K);
   FP4MOE_REQUIRE(a->N > 0 && a->N % 32 == 0 && (a->stage == 2 || a->N % 64 == 0),
                  "fp4_grouped_gemm: N=%d (stage %d)", a->N, a->stage);
@@ -122,6 +133,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: FP8 needs w_channel_scale");
   FP4MOE_REQUIRE(a->afmt != FP4MOE_A_MXFP4 || a->a_scale,
                  "fp4_grouped_gemm: MXFP4 activations need a_scale");
+  FP4MOE_REQUIRE(!f16a || a->a_f16_scale, "fp4_grouped_gemm: f16 activations need a_f16_scale");
   FP4MOE_REQUIRE(((uintptr_t)a->w & 15) == 0 && ((uintptr_t)a->a & 15) == 0,
                  "fp4_grouped_gemm: w and a must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
@@ -152,6 +164,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.q_codes = a->out_q;
   p.q_scales = a->out_q_scale;
   p.q_rows = a->out_q_rows;
+  p.a_f16_scale = a->a_f16_scale;
   hipStream_t s = as_stream(stream);
   const int mt = a->max_tiles;
   const int st = a->stage;

@@ -46,6 +46,9 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 struct GemmParams {
   int N, K, n_experts, block_m, gather_div, w_layout, a_layout, a_rows;
@@ -65,6 +68,7 @@ struct GemmParams {
   uint8_t* q_codes;          // stage-1 output quantized (chunk-major), or NULL
   uint8_t* q_scales;
   int q_rows;
+  const float* a_f16_scale;   // FP4MOE_A_F16: the activations' power-of-two factor
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -112,6 +116,25 @@ __device__ __forceinline__ v2bf nv_pair(uint32_t d, float scale, int sel) {
 __device__ __forceinline__ v8bf decode_nv8(uint32_t d, float scale) {
   return cat8(nv_pair(d, scale, 0), nv_pair(d, scale, 1), nv_pair(d, scale, 2),
               nv_pair(d, scale, 3));
+}
+
+// NVFP4 in f16: eight E2M1 values of dword `d` (element 2i in the low nibble
+// of byte i) times the E4M3 block scale given as a pair (sb, sb).  Both
+// factors and the product (at most 5 significant bits, 2^-10 .. 2688) are
+// exact in f16, so one conversion and one packed f16 multiply per pair.
+__device__ __forceinline__ v8h decode_nv8_f16(uint32_t d, v2h sb2) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sb2;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sb2;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sb2;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sb2;
+  const v4h lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const v4h hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// An E4M3 byte as the f16 pair (v, v) (exact).
+__device__ __forceinline__ v2h e4m3_pair_f16(uint32_t byte) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte | (byte << 8), 1.0f, false);
 }
 
 // Eight bf16 weights from two dwords of E4M3 codes (exact).

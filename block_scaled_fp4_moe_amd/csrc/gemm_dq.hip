@@ -23,13 +23,13 @@ __device__ __forceinline__ uint4 stream_load16(const uint8_t* ptr) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(ptr)));
 }
 
-template <int WFMT, int AFMT, int STAGE, int MB, int NG, int U, int WPE>
-__global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
+template <int WFMT, int AFMT, int STAGE, int MB, int NG, int U, int WPE, int NW>
+__global__ __launch_bounds__(64 * NW, WPE) void dq_gemm_kernel(GemmParams p) {
   static_assert(STAGE == 2 || NG % 2 == 0, "stage 1 pairs gate and up groups");
   constexpr int NGH = NG / 2;
   constexpr int NV = MB * NG * 4;  // accumulator floats per lane
   constexpr int OUT_COLS = (STAGE == 1) ? NGH * 16 : NG * 16;   // output columns per item
-  __shared__ float red[3][NV][64];
+  __shared__ float red[NW - 1][NV][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -114,14 +114,14 @@ __global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int ng = 0; ng < NG; ++ng) acc[mb][ng] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    for (int c0 = wave; c0 < nkc; c0 += 4 * U) {
+    for (int c0 = wave; c0 < nkc; c0 += NW * U) {
       uint4 wv[U][NG][2];
       float sc[U][NG][2];
       uint4 a4[U][MB][4];
       float asc[U][MB];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int c = c0 + 4 * u;
+        const int c = c0 + NW * u;
         if (c >= nkc) break;
         const int blk = c * 4 + g;
 #pragma unroll
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (c0 + 4 * u >= nkc) break;
+        if (c0 + NW * u >= nkc) break;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           v8bf b[NG];
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
       }
     }
 
-    // K reduction over the four waves, in wave order.
+    // K reduction over the NW waves, in wave order.
     if (wave > 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
-      for (int w = 0; w < 3; ++w)
+      for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -247,15 +247,18 @@ __global__ __launch_bounds__(256, WPE) void dq_gemm_kernel(GemmParams p) {
   }
 }
 
-template <int WFMT, int AFMT, int STAGE, int MB, int NG, int U, int WPE>
+template <int WFMT, int AFMT, int STAGE, int MB, int NG, int U, int WPE, int NW = 4>
 static void launch_dq_cfg(const GemmParams& p, int max_tiles, hipStream_t s) {
   const int out_cols = (STAGE == 1) ? (NG / 2) * 16 : NG * 16;
   const int n_nb = ((STAGE == 1) ? p.N / 2 : p.N) / out_cols;
   const int64_t work = (int64_t)max_tiles * n_nb;
-  const int cap = grid_cap();
+  // Up to 32 workgroups per CU: each takes about one work item, so the
+  // hardware dispatcher balances the items as workgroups finish (measured
+  // faster than fewer workgroups looping over several items).
+  const int cap = grid_cap() * 4;
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((dq_gemm_kernel<WFMT, AFMT, STAGE, MB, NG, U, WPE>), dim3(grid), dim3(256),
-                     0, s, p);
+  hipLaunchKernelGGL((dq_gemm_kernel<WFMT, AFMT, STAGE, MB, NG, U, WPE, NW>), dim3(grid),
+                     dim3(64 * NW), 0, s, p);
 }
 
 template <int WFMT, int AFMT, int STAGE>

@@ -36,6 +36,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dqt_gemm_kernel(GemmParams p) {
   constexpr int OUT_PER_WAVE = (STAGE == 1) ? (NGW / 2) * 16 : NGW * 16;
   constexpr int OUT_PER_WG = NW * OUT_PER_WAVE;
   constexpr bool AMX = AFMT == FP4MOE_A_MXFP4;
+  constexpr bool AF16 = AFMT == FP4MOE_A_F16;           // f16 activations, NVFP4 weights
+  static_assert(!AF16 || (WFMT == FP4MOE_W_NVFP4 && NGW == 4), "f16 path: NVFP4, 4 groups");
   constexpr bool W8 = WFMT == FP4MOE_W_FP8;
   constexpr int WFRAG = W8 ? 2048 : 1024;             // one 16-row x 128-K weight fragment
   constexpr int SPB = (WFMT == FP4MOE_W_MXFP4) ? 1 : 2;   // scale bytes per lane per group
@@ -155,6 +157,12 @@ __global__ __launch_bounds__(64 * NW, 1) void dqt_gemm_kernel(GemmParams p) {
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int q = 0; q < NGW; ++q) acc[mb][q] = v4f{0.f, 0.f, 0.f, 0.f};
+    // f16 path: 32x32 tiles, [32-row M block][32 weight rows = 2 groups]
+    v16f acc2[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc2[i][j] = v16f{};
 
     for (int c = 0; c < S - 1 && c < nkc; ++c) issue(c);
     for (int c = 0; c < nkc; ++c) {
@@ -164,6 +172,68 @@ __global__ __launch_bounds__(64 * NW, 1) void dqt_gemm_kernel(GemmParams p) {
       if (c + S - 1 < nkc) issue(c + S - 1);
 
       const uint8_t* st = smem + (c % S) * STAGE_BYTES;
+      if constexpr (AF16) {
+        // 32x32x16 f16 MFMA.  K step u (0..7) of lane half hh = l/32 takes
+        // elements 16*hh + 8*(u%2) .. +7 of 32-element block u/2: for the
+        // weights, dword 2*hh + u%2 of fragment piece (l%16) + 16*(u/2) of
+        // group 2*nb2 + (l%32)/16 -- one NVFP4 block per (u/2, hh), so one
+        // scale -- and for the activations the matching 8 values of row
+        // l%32 of M block mb2.
+        const int l32 = lane & 31, hh = lane >> 5;
+        // every LDS read of the chunk first (their latencies overlap), then
+        // the decode of block kb + 1 runs under the MFMAs of block kb
+        uint2 wd[4][2];
+        uint32_t sbyte[4][2];
+        v8h av[8][2];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int nb2 = 0; nb2 < 2; ++nb2) {
+            const int q = 2 * nb2 + (l32 >> 4);
+            const int piece = (l32 & 15) + 16 * kb;
+            wd[kb][nb2] = *reinterpret_cast<const uint2*>(
+                st + OFF_B + (wave * NGW + q) * WFRAG + piece * 16 + 8 * hh);
+            sbyte[kb][nb2] =
+                st[OFF_BS + (wave * 2 + q / RUN) * RS + (q % RUN) * 128 + piece * 2 + hh];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int mb2 = 0; mb2 < 2; ++mb2)
+            av[u][mb2] = *reinterpret_cast<const v8h*>(
+                st + ((2 * mb2 + (l32 >> 4)) * 4 + (u >> 1)) * 1024 +
+                ((l32 & 15) + 16 * (2 * hh + (u & 1))) * 16);
+        // keep the reads here: the compiler would otherwise sink each one to
+        // its first use and expose the LDS latency once per K step
+        asm volatile("" : "+v"(av[0][0]), "+v"(av[0][1]), "+v"(av[1][0]), "+v"(av[1][1]),
+                     "+v"(av[2][0]), "+v"(av[2][1]), "+v"(av[3][0]), "+v"(av[3][1]),
+                     "+v"(av[4][0]), "+v"(av[4][1]), "+v"(av[5][0]), "+v"(av[5][1]),
+                     "+v"(av[6][0]), "+v"(av[6][1]), "+v"(av[7][0]), "+v"(av[7][1]));
+        asm volatile("" : "+v"(wd[0][0]), "+v"(wd[0][1]), "+v"(wd[1][0]), "+v"(wd[1][1]),
+                     "+v"(wd[2][0]), "+v"(wd[2][1]), "+v"(wd[3][0]), "+v"(wd[3][1]),
+                     "+v"(sbyte[0][0]), "+v"(sbyte[0][1]), "+v"(sbyte[1][0]), "+v"(sbyte[1][1]),
+                     "+v"(sbyte[2][0]), "+v"(sbyte[2][1]), "+v"(sbyte[3][0]), "+v"(sbyte[3][1]));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          v8h bq[2][2];
+#pragma unroll
+          for (int nb2 = 0; nb2 < 2; ++nb2) {
+            const v2h sb2 = e4m3_pair_f16(sbyte[kb][nb2]);
+            bq[nb2][0] = decode_nv8_f16(wd[kb][nb2].x, sb2);
+            bq[nb2][1] = decode_nv8_f16(wd[kb][nb2].y, sb2);
+          }
+#pragma unroll
+          for (int u2 = 0; u2 < 2; ++u2)
+#pragma unroll
+            for (int mb2 = 0; mb2 < 2; ++mb2)
+#pragma unroll
+              for (int nb2 = 0; nb2 < 2; ++nb2)
+                acc2[mb2][nb2] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    av[2 * kb + u2][mb2], bq[nb2][u2], acc2[mb2][nb2], 0, 0, 0);
+        }
+        continue;
+      }
       // this wave's weight fragments and scales for the chunk
       uint4 wv[NGW][W8 ? 2 : 1];
       float sc[NGW][2];
@@ -228,6 +298,36 @@ __global__ __launch_bounds__(64 * NW, 1) void dqt_gemm_kernel(GemmParams p) {
       else if (WFMT == FP4MOE_W_FP8) cs[q] = p.w_channel_scale[(int64_t)e * p.N + wrow];
       else cs[q] = 1.0f;
     }
+    if constexpr (AF16) {
+      // 32x32 result layout: element i of lane l is row 8*(i/4) + 4*(l/32) +
+      // i%4 of the M block, column l%32 of the two groups
+      const float cs2 = p.w_tensor_scale[e] * *p.a_f16_scale;
+      const int l32 = lane & 31, hh = lane >> 5;
+      const int colw = nb * OUT_PER_WG + wave * OUT_PER_WAVE + l32;
+#pragma unroll
+      for (int mb2 = 0; mb2 < 2; ++mb2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = tile_row0 + 32 * mb2 + 8 * (i / 4) + 4 * hh + (i % 4);
+          if (r >= row_end) continue;
+          if (STAGE == 1) {
+            const float h = silu_mul(acc2[mb2][0][i] * cs2, acc2[mb2][1][i] * cs2);
+            const int64_t o = (int64_t)r * p.ldo + colw;
+            p.out[o] = (uint16_t)f32_to_bf16_rne(h);
+            if (p.out_f32) p.out_f32[o] = h;
+          } else {
+#pragma unroll
+            for (int nb2 = 0; nb2 < 2; ++nb2) {
+              const float y = acc2[mb2][nb2][i] * cs2;
+              const int64_t o = (int64_t)r * p.ldo + colw + 32 * nb2;
+              p.out[o] = (uint16_t)f32_to_bf16_rne(y);
+              if (p.out_f32) p.out_f32[o] = y;
+            }
+          }
+        }
+      }
+      continue;
+    }
     const int col0 = nb * OUT_PER_WG + wave * OUT_PER_WAVE + r16;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -276,13 +376,13 @@ static void launch_dqt_stage(const GemmParams& p, int max_tiles, hipStream_t s) 
 // groups, a tile 512 weight rows wide (half the activation copies per weight
 // byte).  Otherwise four waves of four groups.
 static bool wide_dqt(int wfmt, int afmt, int stage, int n_out) {
-  return wfmt != FP4MOE_W_FP8 && afmt == FP4MOE_A_BF16 && n_out % (stage == 1 ? 256 : 512) == 0;
+  return wfmt != FP4MOE_W_FP8 && afmt != FP4MOE_A_MXFP4 && n_out % (stage == 1 ? 256 : 512) == 0;
 }
 
 template <int WFMT, int AFMT>
 static void launch_dqt_fmt(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
   const int n_out = stage == 1 ? p.N / 2 : p.N;
-  if constexpr (WFMT != FP4MOE_W_FP8 && AFMT == FP4MOE_A_BF16) {
+  if constexpr (WFMT != FP4MOE_W_FP8 && AFMT != FP4MOE_A_MXFP4) {
     if (wide_dqt(WFMT, AFMT, stage, n_out)) {
       if (stage == 1) launch_dqt_stage<WFMT, AFMT, 1, 4, 8>(p, max_tiles, s);
       else launch_dqt_stage<WFMT, AFMT, 2, 4, 8>(p, max_tiles, s);
@@ -301,7 +401,9 @@ bool dqt_supported(const GemmParams& p, int stage) {
 
 void launch_dqt_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
                      hipStream_t s) {
-  if (afmt == FP4MOE_A_BF16) {
+  if (afmt == FP4MOE_A_F16) {
+    launch_dqt_fmt<FP4MOE_W_NVFP4, FP4MOE_A_F16>(p, stage, max_tiles, s);
+  } else if (afmt == FP4MOE_A_BF16) {
     if (wfmt == FP4MOE_W_MXFP4) launch_dqt_fmt<FP4MOE_W_MXFP4, FP4MOE_A_BF16>(p, stage, max_tiles, s);
     else if (wfmt == FP4MOE_W_NVFP4) launch_dqt_fmt<FP4MOE_W_NVFP4, FP4MOE_A_BF16>(p, stage, max_tiles, s);
     else launch_dqt_fmt<FP4MOE_W_FP8, FP4MOE_A_BF16>(p, stage, max_tiles, s);

@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const uint16_t* __restr
 __global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
     const uint16_t* __restrict__ x, int M, int K, const int32_t* __restrict__ row_count,
     const float* __restrict__ ts_in, const uint32_t* __restrict__ ws, uint16_t* __restrict__ y,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ ts_out,
+    uint16_t* __restrict__ y16, float* __restrict__ y16_scale) {
   float s_t;
   if (ts_in) {
     s_t = *ts_in;
@@ -173,6 +174,12 @@ __global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
     s_t = amax_t > 0.f ? __fdiv_rn(amax_t, 2688.f) : 1.f;
   }
   if (ts_out && blockIdx.x == 0 && threadIdx.x == 0) *ts_out = s_t;
+  // f16 operand form: y * 2^-p with 2^p the power of two at or below s_t
+  uint32_t pbits = __float_as_uint(s_t) & 0x7f800000u;
+  if (pbits == 0) pbits = 0x00800000u;
+  const float p2 = __uint_as_float(pbits);
+  const float inv_p2 = __fdiv_rn(1.f, p2);                   // exact: a power of two
+  if (y16_scale && blockIdx.x == 0 && threadIdx.x == 0) *y16_scale = p2;
   const float denom = __fmul_rn(6.f, s_t);
   const int rows = row_count ? min(M, *row_count) : M;
   const int64_t total = (int64_t)rows * (K / 8);
@@ -195,6 +202,7 @@ __global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
     const float d = __fmul_rn(sb, s_t);
     uint32_t packed = 0;
     uint32_t yo[4] = {0, 0, 0, 0};
+    uint32_t ho[4] = {0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t h = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
@@ -211,9 +219,13 @@ __global__ __launch_bounds__(256) void nvfp4_qdq_kernel(
       }
       packed |= (mag | (sign << 3)) << (4 * i);
       yo[i >> 1] |= ybits << (16 * (i & 1));
+      const _Float16 hv = (_Float16)(bf16_to_f32(ybits) * inv_p2);   // exact (see header)
+      const uint32_t hb = __builtin_bit_cast(uint16_t, hv) | (ybits & 0x8000u);   // keep -0
+      ho[i >> 1] |= hb << (16 * (i & 1));
     }
     if (active) {
-      reinterpret_cast<uint4*>(y)[c] = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+      if (y) reinterpret_cast<uint4*>(y)[c] = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+      if (y16) reinterpret_cast<uint4*>(y16)[c] = make_uint4(ho[0], ho[1], ho[2], ho[3]);
       if (codes) reinterpret_cast<uint32_t*>(codes)[c] = packed;
       if (scales && (c & 1) == 0) scales[c / 2] = (uint8_t)scode;
     }
@@ -274,14 +286,15 @@ extern "C" size_t nvfp4_qdq_workspace(void) { return 256; }
 
 extern "C" int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
                          const float* tensor_scale_in, uint16_t* y, uint8_t* codes,
-                         uint8_t* scales_e4m3, float* tensor_scale_out, void* workspace,
-                         size_t workspace_bytes, void* stream) {
+                         uint8_t* scales_e4m3, float* tensor_scale_out, uint16_t* y_f16,
+                         float* y_f16_scale, void* workspace, size_t workspace_bytes,
+                         void* stream) {
   FP4MOE_REQUIRE(M >= 0 && K > 0 && K % 16 == 0, "nvfp4_qdq: M=%d K=%d (K %% 16 != 0)", M, K);
   if (M == 0) return FP4MOE_OK;
-  FP4MOE_REQUIRE(x && y, "nvfp4_qdq: null pointer");
+  FP4MOE_REQUIRE(x && (y || y_f16), "nvfp4_qdq: null pointer");
   FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)y & 15) == 0 &&
-                     ((uintptr_t)codes & 3) == 0,
-                 "nvfp4_qdq: x, y must be 16-byte and codes 4-byte aligned");
+                     ((uintptr_t)y_f16 & 15) == 0 && ((uintptr_t)codes & 3) == 0,
+                 "nvfp4_qdq: x, y, y_f16 must be 16-byte and codes 4-byte aligned");
   FP4MOE_CHECK_DEVICE();
   hipStream_t s = as_stream(stream);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
@@ -298,6 +311,7 @@ extern "C" int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_cou
                        ws);
   }
   hipLaunchKernelGGL(nvfp4_qdq_kernel, dim3(grid_for(chunks, 256)), dim3(256), 0, s, x, M, K,
-                     row_count, tensor_scale_in, ws, y, codes, scales_e4m3, tensor_scale_out);
+                     row_count, tensor_scale_in, ws, y, codes, scales_e4m3, tensor_scale_out,
+                     y_f16, y_f16_scale);
   return check_launch("nvfp4_qdq");
 }

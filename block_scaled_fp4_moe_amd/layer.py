@@ -14,7 +14,7 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (A_BF16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
+from . import (A_BF16, A_F16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
                LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle, moe_combine,
                moe_permute, moe_permute_max_tiles, moe_route, moe_route_permute,
                mxfp4_quant_1x32,
@@ -76,6 +76,12 @@ class MoELayer:
         self.chunked = (cfg.afmt == "mx" and cfg.fragment_layout and
                         ((cfg.wfmt == "mx" and cfg.block_m in (128, 192, 256)) or
                          (cfg.wfmt == "fp8" and cfg.block_m == 192)))
+        # NVFP4 with 64-row tiles: activations in the f16 operand form of
+        # nvfp4_qdq (E2M1 x E4M3 weights decode to f16 with one packed multiply
+        # per pair, and the 32x32 f16 MFMA runs at twice the 16x16 bf16 rate)
+        n13, n2 = cfg.I, cfg.H
+        self.f16a = (cfg.afmt == "nvfp4" and cfg.wfmt == "nvfp4" and cfg.block_m == 64 and
+                     cfg.fragment_layout and n13 % 128 == 0 and n2 % 256 == 0)
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
@@ -115,8 +121,11 @@ class MoELayer:
             b["hq"] = torch.empty((P, c.I // 2), dtype=torch.uint8, device=dev)
             b["hs"] = torch.empty((P, c.I // 32), dtype=torch.uint8, device=dev)
         elif c.afmt == "nvfp4":
-            b["xq"] = torch.empty((T, c.H), dtype=torch.bfloat16, device=dev)
-            b["hq"] = torch.empty((P, c.I), dtype=torch.bfloat16, device=dev)
+            dt = torch.float16 if self.f16a else torch.bfloat16
+            b["xq"] = torch.empty((T, c.H), dtype=dt, device=dev)
+            b["hq"] = torch.empty((P, c.I), dtype=dt, device=dev)
+            b["xs"] = torch.empty(1, dtype=torch.float32, device=dev)
+            b["hs"] = torch.empty(1, dtype=torch.float32, device=dev)
         self._bufs[T] = b
         return b
 
@@ -159,6 +168,10 @@ class MoELayer:
         elif c.afmt == "mx":
             mxfp4_quant_1x32(x, codes=b["xq"], scales=b["xs"], stream=stream)
             a1, a1s, af = b["xq"], b["xs"], A_MXFP4
+        elif c.afmt == "nvfp4" and self.f16a:
+            nvfp4_qdq(x, y_f16=b["xq"], y_f16_scale=b["xs"], no_y=True,
+                      workspace=self.nvfp4_ws, stream=stream)
+            a1, a1s, af = b["xq"], None, A_F16
         elif c.afmt == "nvfp4":
             nvfp4_qdq(x, y=b["xq"], workspace=self.nvfp4_ws, stream=stream)
             a1, a1s, af = b["xq"], None, A_BF16
@@ -171,10 +184,11 @@ class MoELayer:
         # then written only when the caller keeps the intermediates)
         fused_q = self.chunked and c.block_m == 192
         qkw = dict(out_q=b["hq"], out_q_scale=b["hs"], no_out=not keep) if fused_q else {}
+        f16kw = dict(a_f16_scale=b["xs"]) if self.f16a else {}
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
                          out=b["h"] if (keep or not fused_q) else None, w_layout=self.layout,
-                         a_layout=a_layout, stream=stream, **qkw, **gather)
+                         a_layout=a_layout, stream=stream, **qkw, **gather, **f16kw)
         tick("quant2")
         if fused_q:
             a2, a2s = b["hq"], b["hs"]
@@ -186,6 +200,10 @@ class MoELayer:
             mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
                              stream=stream)
             a2, a2s = b["hq"], b["hs"]
+        elif c.afmt == "nvfp4" and self.f16a:
+            nvfp4_qdq(b["h"], row_count=n_rows, y_f16=b["hq"], y_f16_scale=b["hs"], no_y=True,
+                      workspace=self.nvfp4_ws, stream=stream)
+            a2, a2s = b["hq"], None
         elif c.afmt == "nvfp4":
             nvfp4_qdq(b["h"], row_count=n_rows, y=b["hq"], workspace=self.nvfp4_ws,
                       stream=stream)
@@ -195,9 +213,11 @@ class MoELayer:
         ts2 = w.get("w2_ts") if c.wfmt == "nvfp4" else None
         cs2 = w["w2_scale"] if c.wfmt == "fp8" else None
         tick("stage2")
+        f16kw = dict(a_f16_scale=b["hs"]) if self.f16a else {}
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
                          c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
-                         out=b["y"], w_layout=self.layout, a_layout=a_layout, stream=stream)
+                         out=b["y"], w_layout=self.layout, a_layout=a_layout, stream=stream,
+                         **f16kw)
         tick("combine")
         moe_combine(b["y"], perm["pair_pos"], b["topk_w"], c.topk, c.n_shared, out=b["out"],
                     stream=stream)

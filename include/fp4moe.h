@@ -60,7 +60,9 @@ enum {
 /* Activation formats of fp4_grouped_gemm. */
 enum {
   FP4MOE_A_BF16 = 0,   /* bf16 [rows, K]: weights are decoded to bf16 inside the GEMM tile  */
-  FP4MOE_A_MXFP4 = 1   /* E2M1 codes [rows, K/2] + E8M0 [rows, K/32]: gfx950 scaled MFMA    */
+  FP4MOE_A_MXFP4 = 1,  /* E2M1 codes [rows, K/2] + E8M0 [rows, K/32]: gfx950 scaled MFMA    */
+  FP4MOE_A_F16 = 2     /* f16 [rows, K] times the power of two *a_f16_scale: the f16 form
+                          that nvfp4_qdq writes; NVFP4 weights decoded to f16 in the tile  */
 };
 
 /* Layouts of MXFP4 activations (see mxfp4_quant_1x32_chunked). */
@@ -184,12 +186,19 @@ int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t ldx, const
  *   y = bf16(f32(q*sb) * s_t).
  * x, y bf16 [M,K] (K % 16 == 0); codes [M,K/2], scales_e4m3 [M,K/16] and
  * tensor_scale_out [1] are optional (NULL).  row_count as in mxfp4_quant_1x32.
- * The dynamic scale needs a workspace of nvfp4_qdq_workspace() bytes.
+ * y_f16 (optional, f16 [M,K]) receives y * 2^-p and y_f16_scale (optional,
+ * [1]) receives 2^p, where 2^p <= s_t < 2^(p+1) (2^-126 for a zero or
+ * subnormal s_t): the operand form of FP4MOE_A_F16.  For a positive finite
+ * s_t every y * 2^-p is a multiple of 2^-17 below 5400 (|q*sb| lies in
+ * [2^-10, 2688] and y has at most 8 significant bits), so y_f16 holds y
+ * exactly.  y may be NULL when y_f16 is given.  The dynamic scale needs a workspace of
+ * nvfp4_qdq_workspace() bytes.
  */
 size_t nvfp4_qdq_workspace(void);
 int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
               const float* tensor_scale_in, uint16_t* y, uint8_t* codes, uint8_t* scales_e4m3,
-              float* tensor_scale_out, void* workspace, size_t workspace_bytes, void* stream);
+              float* tensor_scale_out, uint16_t* y_f16, float* y_f16_scale, void* workspace,
+              size_t workspace_bytes, void* stream);
 
 /*
  * fp4_grouped_gemm -- one GEMM stage over all expert segments.
@@ -224,6 +233,11 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * stage-2 activations of [ATOM] "Stage B" without a separate pass over h;
  * out may then be NULL (h not written in bf16).  Rows past a segment's end
  * are not written.
+ * afmt FP4MOE_A_F16 (the f16 operand form of nvfp4_qdq; a_f16_scale points
+ * to its power-of-two factor) is taken with NVFP4 fragment-major weights and
+ * block_m 64: E2M1 times E4M3 is exact in f16 (at most 5 significant bits,
+ * magnitudes 2^-10 .. 2688), so the products equal those of the bf16 form
+ * and the factor is applied with the tensor scale in the epilogue.
  */
 typedef struct {
   int stage;               /* 1 or 2                                                */
@@ -256,6 +270,7 @@ typedef struct {
   uint8_t* out_q;          /* optional: stage-1 output as MXFP4 codes, chunked      */
   uint8_t* out_q_scale;    /*   and its E8M0 scales (see below)                     */
   int out_q_rows;          /*   rows per K chunk slab of out_q / out_q_scale        */
+  const float* a_f16_scale;  /* FP4MOE_A_F16: device [1], the power-of-two factor   */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);

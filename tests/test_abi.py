@@ -84,8 +84,11 @@ def test_quant_and_convert_reject_bad_K():
                                                                 None, None, None))
     assert st == 1 and "out_rows" in msg        # without a map every input row needs a slot
     st, msg = _status(lambda lib: lib.nvfp4_qdq(None, 4, 24, None, None, None, None, None, None,
-                                                 None, 0, None))
+                                                 None, None, None, 0, None))
     assert st == 1
+    st, msg = _status(lambda lib: lib.nvfp4_qdq(None, 4, 32, None, None, None, None, None, None,
+                                                 None, None, None, 0, None))
+    assert st == 1 and "null" in msg            # neither y nor y_f16
     st, msg = _status(lambda lib: lib.mxfp4_to_fp8_channel(None, None, 4, 40, None, None, None,
                                                             None, None))
     assert st == 1
@@ -107,7 +110,7 @@ def test_gemm_rejects_unsupported_combinations():
                            None, None, None, None, None, None, a["lda"], None, None, None, None,
                            None, a["ldo"], a.get("out_f32"), a.get("w_layout", 0),
                            a.get("a_layout", 0), a.get("a_rows", 0), a.get("out_q"),
-                           a.get("out_q_scale"), a.get("out_q_rows", 0))
+                           a.get("out_q_scale"), a.get("out_q_rows", 0), a.get("a_f16_scale"))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -156,6 +159,15 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**{**wide, "block_m": 256, "ldo": 256}, **q)[0] == 1
     assert run(**wide, **{**q, "out_q_rows": 4})[0] == 1       # < max_rows
     assert run(**wide, **q, out_f32=256)[0] == 1
+    # f16 activations (the NVFP4 operand form): NVFP4 fragment weights, block_m 64
+    f16 = dict(wfmt=1, afmt=2, block_m=64, w_layout=1, N=512, ldo=256, max_tiles=0)
+    assert run(**f16)[0] == 0
+    assert run(**{**f16, "ldo": 512}, stage=2)[0] == 0
+    assert run(**{**f16, "wfmt": 0})[0] == 1
+    assert run(**{**f16, "block_m": 16})[0] == 1
+    assert run(**{**f16, "w_layout": 0})[0] == 1
+    assert run(**{**f16, "N": 192, "ldo": 96})[0] == 1           # output width 96
+    assert run(afmt=3)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 
 

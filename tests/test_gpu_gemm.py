@@ -95,6 +95,21 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
             qs = qs.copy()
             qs[n_rows:] = 255
         a_kw = dict(a=dev(qc), a_scale=dev(qs), afmt=gpu_lib.A_MXFP4)
+    elif afmt == "f16":
+        # NVFP4 activations in the f16 operand form, made on the host from the
+        # oracle's QDQ: y * 2^-p is exact in f16
+        r = OQ.nvfp4_qdq(xb)
+        s_t = np.float32(r["tensor_scale"])
+        bits = np.array([s_t], np.float32).view(np.uint32)[0] & np.uint32(0x7F800000)
+        p2 = np.array([bits], np.uint32).view(np.float32)[0]
+        a_vals = F.bf16_decode(r["y"])
+        a16 = (a_vals / np.float64(p2)).astype(np.float16)
+        assert np.array_equal(a16.astype(np.float64) * np.float64(p2), a_vals)
+        if poison:
+            a16 = a16.copy()
+            a16[n_rows:] = np.float16("nan")
+        a_kw = dict(a=dev(a16.view(np.int16)).view(torch.float16), afmt=gpu_lib.A_F16,
+                    a_f16_scale=dev(np.array([p2], np.float32)))
     else:
         a_vals = F.bf16_decode(xb)
         if poison:
@@ -194,6 +209,28 @@ DQ_CASES = [
 def test_dq_gemm_parity(gpu_lib, case, layout):
     stage, wfmt, T, topk, E, ns, H, I, bm, seed, skew = case
     run_stage(gpu_lib, stage, wfmt, "bf16", T, topk, E, ns, H, I, bm, seed, skew, layout=layout)
+
+
+F16_CASES = [
+    # stage, T, topk, E, ns, H, I, seed, skew: NVFP4 weights x f16 activations,
+    # 64-row tiles (32x32 f16 MFMA): several tiles per expert with ragged
+    # tails, a shared expert, empty experts, full width, narrow width (4 waves)
+    (1, 60, 4, 8, 0, 512, 256, 61, True),
+    (2, 60, 4, 8, 0, 512, 256, 62, True),
+    (1, 150, 6, 10, 1, 1024, 512, 63, True),
+    (2, 150, 6, 10, 1, 1024, 512, 64, True),
+    (1, 9, 3, 5, 1, 7168, 2048, 65, False),
+    (2, 9, 3, 5, 1, 7168, 2048, 66, False),
+    (1, 40, 2, 6, 0, 256, 128, 67, False),
+    (2, 40, 2, 6, 0, 256, 256, 68, False),
+]
+
+
+@pytest.mark.parametrize("case", F16_CASES)
+def test_nvfp4_f16_activation_gemm(gpu_lib, case):
+    stage, T, topk, E, ns, H, I, seed, skew = case
+    run_stage(gpu_lib, stage, "nvfp4", "f16", T, topk, E, ns, H, I, 64, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT)
 
 
 MX_CASES = [

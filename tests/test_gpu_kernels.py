@@ -313,6 +313,44 @@ def test_nvfp4_qdq_parity(gpu_lib, M, K, static):
     assert_equal(bits_of(y), ref["y"], "y")
 
 
+def _pow2_below(s_t):
+    """2^p <= s_t < 2^(p+1) for a normal float32 s_t (2^-126 for zero / subnormal)."""
+    bits = np.array([s_t], np.float32).view(np.uint32)[0] & np.uint32(0x7F800000)
+    return np.array([max(bits, 0x00800000)], np.uint32).view(np.float32)[0]
+
+
+@pytest.mark.parametrize("M,K,ts", [(64, 7168, None), (33, 2048, 0.0037), (16, 256, 2.0 ** -120),
+                                    (16, 256, 3.0e5), (24, 512, 2.0 ** -130)])
+def test_nvfp4_qdq_f16_form(gpu_lib, M, K, ts):
+    """The f16 operand form: y_f16 * y_f16_scale equals the oracle's y exactly,
+    for dynamic, tiny, large and subnormal tensor scales."""
+    g = np.random.default_rng(M + K)
+    xb = synth.bf16_from_f32(g.standard_normal((M, K)).astype(np.float32) *
+                             np.exp(g.uniform(-3, 3, (M, 1))).astype(np.float32))
+    if ts is not None and ts < 1e-30:
+        xb = synth.bf16_from_f32(F.bf16_decode(xb).astype(np.float32) * np.float32(ts * 1e3))
+    xb[1, :16] = 0
+    xb[2, :16] = 0x8000
+    tsd = None if ts is None else dev(np.array([ts], np.float32))
+    ref = OQ.nvfp4_qdq(xb, tensor_scale_in=None if ts is None else np.float32(ts))
+    p2 = _pow2_below(np.float32(ref["tensor_scale"]))
+    y16 = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    sc = torch.zeros(1, dtype=torch.float32, device="cuda")
+    y = gpu_lib.nvfp4_qdq(bf16_dev(xb), tensor_scale=tsd, y_f16=y16, y_f16_scale=sc)
+    assert_equal(bits_of(y), ref["y"], "y")
+    assert host(sc)[0] == p2
+    want = F.bf16_decode(ref["y"])
+    got = host(y16).astype(np.float64) * np.float64(p2)
+    assert np.array_equal(got, want), "y_f16 * scale != y"
+    assert np.array_equal(np.signbit(host(y16)), np.signbit(want)), "signs of zeros"
+    # without the bf16 output
+    y16b = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    none = gpu_lib.nvfp4_qdq(bf16_dev(xb), tensor_scale=tsd, y_f16=y16b, y_f16_scale=sc,
+                             no_y=True)
+    assert none is None
+    assert np.array_equal(host(y16b).view(np.uint16), host(y16).view(np.uint16))
+
+
 def test_nvfp4_qdq_row_count_and_zero(gpu_lib):
     g = np.random.default_rng(3)
     xb = synth.bf16_from_f32(g.standard_normal((20, 64)).astype(np.float32))
