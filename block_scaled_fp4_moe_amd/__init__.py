@@ -73,6 +73,7 @@ def load():
         "nvfp4_qdq_workspace": ([], S),
         "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, P, P, S, P], I),
         "fp4_grouped_gemm": ([ctypes.POINTER(GemmArgs), P], I),
+        "mxfp4_linear": ([P, P, I, I, I, I64, P, P, I, P, I64, P, P], I),
         "moe_combine": ([P, P, P, I, I, I, I, P, P, P], I),
         "fp4_weight_preshuffle": ([I, I, I, I, P, P, P, P, P], I),
         "mxfp4_to_fp8_channel": ([P, P, I64, I, P, P, P, P, P], I),
@@ -301,6 +302,29 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     0 if out_q is None else out_q.shape[1],
                     None if a_f16_scale is None else a_f16_scale.data_ptr())
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
+    return out
+
+
+def mxfp4_linear(a, a_scale, w, w_scale, a_layout=0, M=None, out=None, out_f32=None,
+                 stream=None):
+    """Dense out = bf16(A . W^T): a / a_scale MXFP4 activations (row-major codes
+    [M, K/2] + scales [M, K/32], or chunk-major [K/128, rows, 64] / [K/128, rows, 4]
+    with a_layout 1 and M <= rows), w / w_scale one fragment-major MXFP4 matrix
+    [N, K/2] / [N, K/32] (fp4_weight_preshuffle of a [1, N, K/2] tensor).
+    Returns out bf16 [M, N]."""
+    lib = load()
+    N, K = w.shape[-2], w.shape[-1] * 2
+    if a_layout == A_LAYOUT_CHUNKED:
+        rows = a.shape[1]
+        M = rows if M is None else M
+        stride = rows
+    else:
+        M = a.shape[0] if M is None else M
+        stride = a.stride(0) * 2
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=_dev(a))
+    _check(lib.mxfp4_linear(_p(a), _p(a_scale), M, K, a_layout, stride, _p(w), _p(w_scale), N,
+                            _p(_u16(out)), out.stride(0), _p(out_f32), _stream(stream)))
     return out
 
 

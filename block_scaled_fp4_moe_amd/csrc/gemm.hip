@@ -138,7 +138,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: w and a must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
 
-  GemmParams p;
+  GemmParams p{};
   p.N = a->N;
   p.K = a->K;
   p.n_experts = a->n_experts;
@@ -173,4 +173,48 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");
+}
+
+extern "C" int mxfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, int M, int K,
+                            int a_layout, int64_t a_stride, const uint8_t* w,
+                            const uint8_t* w_scale, int N, uint16_t* out, int64_t ldo,
+                            float* out_f32, void* stream) {
+  FP4MOE_REQUIRE(M >= 0, "mxfp4_linear: M=%d", M);
+  FP4MOE_REQUIRE(K > 0 && K % 128 == 0, "mxfp4_linear: K=%d not a multiple of 128", K);
+  FP4MOE_REQUIRE(N > 0 && N % 512 == 0, "mxfp4_linear: N=%d not a multiple of 512", N);
+  FP4MOE_REQUIRE(a_layout == FP4MOE_A_LAYOUT_ROWMAJOR || a_layout == FP4MOE_A_LAYOUT_CHUNKED,
+                 "mxfp4_linear: a_layout=%d", a_layout);
+  const bool chunked = a_layout == FP4MOE_A_LAYOUT_CHUNKED;
+  FP4MOE_REQUIRE(chunked ? (a_stride >= M && a_stride <= (1 << 26))
+                         : (a_stride >= K && a_stride % 32 == 0 &&
+                            (int64_t)M * (a_stride / 2) <= (int64_t)0xffffffff),
+                 "mxfp4_linear: a_stride=%lld (M=%d, K=%d, layout %d)", (long long)a_stride, M, K,
+                 a_layout);
+  FP4MOE_REQUIRE(ldo >= N && ldo % 8 == 0, "mxfp4_linear: ldo=%lld", (long long)ldo);
+  if (M == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(a_codes && a_scales && w && w_scale && out, "mxfp4_linear: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)a_codes & 15) == 0 && ((uintptr_t)w & 15) == 0 &&
+                     ((uintptr_t)out & 15) == 0,
+                 "mxfp4_linear: a_codes, w and out must be 16-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  GemmParams p{};
+  p.N = N;
+  p.K = K;
+  p.n_experts = 1;
+  p.block_m = 192;
+  p.gather_div = 1;
+  p.w_layout = FP4MOE_LAYOUT_FRAGMENT;
+  p.a_layout = a_layout;
+  p.a_rows = chunked ? (int)a_stride : 0;
+  p.lda = chunked ? K : a_stride;
+  p.ldo = ldo;
+  p.w = w;
+  p.w_scale = w_scale;
+  p.a = a_codes;
+  p.a_scale = a_scales;
+  p.out = out;
+  p.out_f32 = out_f32;
+  p.dense_rows = M;
+  launch_mx_dense_gemm(p, as_stream(stream));
+  return check_launch("mxfp4_linear");
 }

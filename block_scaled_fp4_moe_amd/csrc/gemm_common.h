@@ -69,6 +69,7 @@ struct GemmParams {
   uint8_t* q_scales;
   int q_rows;
   const float* a_f16_scale;   // FP4MOE_A_F16: the activations' power-of-two factor
+  int dense_rows;             // > 0: one dense matrix of this many rows, no tile list
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -196,6 +197,9 @@ int grid_cap();
 void launch_dq_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,
                     hipStream_t s);
 void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+// Dense MXFP4 x MXFP4 (p.dense_rows rows, one fragment-major weight matrix,
+// stage-2 semantics, 192 x 512 tiles).
+void launch_mx_dense_gemm(const GemmParams& p, hipStream_t s);
 // FP8 weights x MXFP4 activations on the scaled MFMA (block_m 192, fragment weights).
 void launch_mx_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
 // Tiled dq variant (64-row tiles, fragment weights): whether it takes `p`.

@@ -714,7 +714,11 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   const int n_nb = n_out / OUT_PER_WG;
   const int nkc = p.K / 128;
   const int G = p.N / 16;
-  const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
+  // dense mode (p.dense_rows > 0): one matrix, rows [0, dense_rows), the tile
+  // list implicit
+  const bool dense = p.dense_rows > 0;
+  const int64_t n_tiles_all = dense ? (p.dense_rows + BM - 1) / BM : *p.n_tiles;
+  const int64_t n_work = n_tiles_all * n_nb;
   const uint8_t* A = static_cast<const uint8_t*>(p.a);
   const bool chunked = p.a_layout == FP4MOE_A_LAYOUT_CHUNKED;
   const int64_t a_row_bytes = chunked ? 64 : p.lda / 2, a_srow = chunked ? 4 : p.lda / 32;
@@ -746,13 +750,14 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
 
   for (int64_t wi = w_begin + slot; wi < w_end; wi += slots) {
     const int any_tile = (int)(wi / n_nb);
-    const int e = p.tiles[2 * any_tile];
-    const int t0 = any_tile - p.tiles[2 * any_tile + 1];
-    const int m_tiles = (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
+    const int e = dense ? 0 : p.tiles[2 * any_tile];
+    const int t0 = dense ? 0 : any_tile - p.tiles[2 * any_tile + 1];
+    const int seg0 = dense ? 0 : p.offsets[e], seg1 = dense ? p.dense_rows : p.offsets[e + 1];
+    const int m_tiles = (seg1 - seg0 + BM - 1) / BM;
     const int local = (int)(wi - (int64_t)t0 * n_nb);
     const int nb = local / m_tiles, mt = local - nb * m_tiles;
-    const int tile_row0 = p.offsets[e] + mt * BM;
-    const int row_end = min(p.offsets[e + 1], tile_row0 + BM);
+    const int tile_row0 = seg0 + mt * BM;
+    const int row_end = min(seg1, tile_row0 + BM);
 
     auto src_row = [&](int r) -> int64_t {
       if (r >= row_end) return 0;
@@ -1069,6 +1074,10 @@ static void launch_mx(const GemmParams& p, int max_tiles, hipStream_t s) {
       else launch_mx_lds<STAGE, 8>(p, max_tiles, s);
       break;
   }
+}
+
+void launch_mx_dense_gemm(const GemmParams& p, hipStream_t s) {
+  launch_mx_wide<2, false>(p, (p.dense_rows + 191) / 192, s);
 }
 
 void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {

@@ -276,6 +276,25 @@ typedef struct {
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);
 
 /*
+ * mxfp4_linear -- dense MXFP4 x MXFP4 linear layer: out = bf16(A . W^T).
+ * [ATOM] "Stage C: MXFP4 Linear GEMM": activations quantized 1x32 on the fly
+ * times a pre-shuffled MXFP4 weight on the gfx950 scaled MFMA -- the same
+ * 192 x 512 tile as the prefill MoE GEMM, with one matrix and every row.
+ *   A: M rows of MXFP4 activations; a_layout FP4MOE_A_LAYOUT_CHUNKED: the
+ *      output of mxfp4_quant_1x32_chunked with out_rows = a_stride >= M;
+ *      FP4MOE_A_LAYOUT_ROWMAJOR: codes [M, a_stride/2] + E8M0 [M, a_stride/32]
+ *      (a_stride = row stride in elements, M * a_stride / 2 < 2^32).
+ *   W: one [N, K] MXFP4 matrix in the fragment-major layout
+ *      (fp4_weight_preshuffle with E = 1): codes and E8M0 scales.
+ *   out: bf16 [M, ldo]; out_f32 (optional) the float32 values before rounding.
+ * K % 128 == 0, N % 512 == 0, ldo % 8 == 0; a_codes, w and out 16-byte
+ * aligned.  Device pointers owned by the caller; nothing is allocated.
+ */
+int mxfp4_linear(const uint8_t* a_codes, const uint8_t* a_scales, int M, int K, int a_layout,
+                 int64_t a_stride, const uint8_t* w, const uint8_t* w_scale, int N, uint16_t* out,
+                 int64_t ldo, float* out_f32, void* stream);
+
+/*
  * fp4_weight_preshuffle -- rewrite static expert weights into the
  * fragment-major layout (FP4MOE_LAYOUT_FRAGMENT) that fp4_grouped_gemm
  * streams with one contiguous KiB per wavefront load.

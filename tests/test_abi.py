@@ -24,10 +24,10 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
               "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked",
-              "moe_route_permute"]:
+              "moe_route_permute", "mxfp4_linear"]:
         assert n in names
     for n in names:
         assert getattr(lib, n) is not None
@@ -169,6 +169,19 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**{**f16, "N": 192, "ldo": 96})[0] == 1           # output width 96
     assert run(afmt=3)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
+
+
+def test_linear_rejects_bad_arguments():
+    def run(M=8, K=256, layout=0, stride=256, N=512, ldo=512):
+        return _status(lambda lib: lib.mxfp4_linear(None, None, M, K, layout, stride, None, None,
+                                                    N, None, ldo, None, None))
+    assert run(M=0)[0] == 0                     # nothing to do
+    assert run()[0] == 1                        # null pointers
+    for bad in (dict(K=96), dict(N=256), dict(layout=2), dict(ldo=516), dict(ldo=256),
+                dict(stride=128), dict(layout=1, stride=4), dict(M=-1)):
+        st, msg = run(**bad)
+        assert st == 1 and "mxfp4_linear" in msg, bad
+    assert run(M=0, layout=1, stride=0)[0] == 0
 
 
 def test_preshuffle_rejects_bad_shapes():

@@ -367,3 +367,56 @@ def test_preshuffle_layout(gpu_lib, wfmt):
     assert np.array_equal(host(c), codes_ref)
     if wfmt != "fp8":
         assert np.array_equal(host(sc), scales_ref)
+
+
+# ------------------------------------------------------------------ dense MXFP4 linear
+
+LINEAR_CASES = [
+    # M, N, K, a_layout, seed: single rows, ragged 192-row tails, several column
+    # blocks, both activation layouts, the hidden width as K
+    (1, 512, 128, 0, 81), (37, 512, 256, 1, 82), (192, 1024, 512, 0, 83),
+    (500, 1536, 1024, 1, 84), (2000, 512, 7168, 0, 85), (385, 2048, 2048, 1, 86),
+]
+
+
+@pytest.mark.parametrize("case", LINEAR_CASES)
+def test_mxfp4_linear_parity(gpu_lib, case):
+    M, N, K, a_layout, seed = case
+    rng = np.random.default_rng(seed)
+    xb = synth.bf16_from_f32(rng.standard_normal((M, K), dtype=np.float32))
+    qc, qs = OQ.mxfp4_quant_1x32(xb)
+    a_vals = F.mxfp4_dequant(qc, qs)
+    wd = make_weights(rng, 1, N, K, "mx")
+    fc, fs = gpu_lib.fp4_weight_preshuffle(gpu_lib.WFMT["mx"], dev(wd["codes"]), dev(wd["scale"]))
+    if a_layout == 1:
+        rows = M + 5                     # a slab taller than M: rows past M are never read
+        cpad = np.vstack([qc, np.full((rows - M, K // 2), 0x77, np.uint8)])
+        spad = np.vstack([qs, np.full((rows - M, K // 32), 255, np.uint8)])
+        cc, cs = chunk_major(cpad, spad)
+        a, a_s = dev(cc), dev(cs)
+    else:
+        a, a_s = dev(qc), dev(qs)
+    out_f32 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = gpu_lib.mxfp4_linear(a, a_s, fc[0], fs[0], a_layout=a_layout, M=M, out_f32=out_f32)
+    ref = OG.grouped_stage(2, a_vals, np.array([0, M]), lambda e: oracle_weight(wd, "mx", 0),
+                           rounding=False)
+    assert_float_close(host(out_f32), ref, "mxfp4_linear f32")
+    assert_bf16_close(bits_of(out), ref, "mxfp4_linear bf16")
+
+
+def test_mxfp4_linear_exact_special_case(gpu_lib):
+    """E8M0 = 127 weights and activations on {0, +-.5, +-1, +-1.5, +-2}: every
+    product and partial sum is exact, so the float32 output equals the oracle
+    bit for bit."""
+    rng = np.random.default_rng(87)
+    M, N, K = 250, 1024, 2048
+    vals = np.array([0, .5, 1, 1.5, 2, -.5, -1, -1.5, -2], np.float32)
+    xb = synth.bf16_from_f32(vals[rng.integers(0, len(vals), (M, K))])
+    qc, qs = OQ.mxfp4_quant_1x32(xb)
+    codes = rng.integers(0, 256, (1, N, K // 2), dtype=np.uint8)
+    scale = np.full((1, N, K // 32), 127, np.uint8)
+    fc, fs = gpu_lib.fp4_weight_preshuffle(gpu_lib.WFMT["mx"], dev(codes), dev(scale))
+    out_f32 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.mxfp4_linear(dev(qc), dev(qs), fc[0], fs[0], out_f32=out_f32)
+    ref = F.mxfp4_dequant(qc, qs) @ OG.dequant_expert("mx", codes[0], scale[0]).T
+    assert np.array_equal(host(out_f32).astype(np.float64), ref)
