@@ -141,7 +141,9 @@ class MoELayer:
         k = c.topk + c.n_shared
         b = self._buffers(T)
         tick("route")
-        if T <= ROUTE_PERMUTE_MAX_TOKENS and T * k <= 1024:
+        # (one launch only when every routed expert is local: the fused call
+        # permutes over the same E it routes over)
+        if T <= ROUTE_PERMUTE_MAX_TOKENS and T * k <= 1024 and logits.shape[1] == c.E:
             # decode sizes: routing and permutation in one launch
             _, _, perm = moe_route_permute(logits, bias, c.n_group, c.topk_group, c.topk,
                                            c.n_shared, c.block_m, c.renormalize, c.routed_scale,

@@ -144,3 +144,44 @@ def test_layer_nvfp4_full_width(gpu_lib, block_m):
 @pytest.mark.parametrize("block_m", [32, 64, 192])
 def test_layer_fp8_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", block_m)
+
+
+@pytest.mark.parametrize("T", [8, 64])
+def test_layer_expert_parallel_share(gpu_lib, T):
+    """One of eight expert-parallel ranks: routed experts [0, 48) and the shared
+    expert on this GPU, routing over all 384 experts, pairs routed elsewhere
+    dropped by the permutation (and skipped by the combine)."""
+    w = synth.WORKLOADS["decode"]
+    E_loc = w.E // 8
+    logits = synth.router_logits(w, T, 3)
+    bias = synth.router_bias(w)
+    xb = synth.activations(w, T, 3)
+    H, I = w.H, w.I
+    Et = E_loc + w.n_shared
+    np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+    dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
+                 w13_scale=torch.empty((Et, 2 * I, H // 32), dtype=torch.uint8, device="cuda"),
+                 w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
+                 w2_scale=torch.empty((Et, H, I // 32), dtype=torch.uint8, device="cuda"))
+    for le, ge in enumerate(list(range(E_loc)) + list(range(w.E, w.E + w.n_shared))):
+        c13, s13 = synth.expert_mx(w, ge, 13)
+        c2, s2 = synth.expert_mx(w, ge, 2)
+        np_w["w13"][le], np_w["w13_scale"][le], np_w["w2"][le], np_w["w2_scale"][le] = \
+            c13, s13, c2, s2
+        dev_w["w13"][le].copy_(torch.from_numpy(c13))
+        dev_w["w13_scale"][le].copy_(torch.from_numpy(s13))
+        dev_w["w2"][le].copy_(torch.from_numpy(c2))
+        dev_w["w2_scale"][le].copy_(torch.from_numpy(s2))
+    cfg = gpu_lib.LayerConfig(H=H, I=I, E=E_loc, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx",
+                              block_m=16)
+    layer = gpu_lib.MoELayer(cfg, dev_w)
+    b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
+    ref = OL.moe_layer(xb, logits, bias, np_w, E=E_loc, n_shared=w.n_shared, n_group=w.n_group,
+                       topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx", block_m=16)
+    assert_equal(host(b["topk_ids"]), ref["topk_ids"].reshape(T, w.topk), "topk_ids")
+    assert_equal(host(b["perm"]["pair_pos"]), ref["perm"]["pair_pos"], "pair_pos")
+    assert int(host(b["perm"]["n_dropped"])[0]) == ref["perm"]["n_dropped"] > 0
+    n = int(ref["perm"]["expert_offsets"][-1])
+    assert_bf16_close(bits_of(b["h"])[:n], ref["h"], "h")
+    assert_bf16_close(bits_of(b["out"]), ref["out"], "out")
