@@ -89,21 +89,40 @@ def build_weights(w, experts, wfmt, torch_empty_experts):
     return np_w, dev_w
 
 
+# The inputs, weights and oracle results of the last (workload, T, seed,
+# formats) case: the values do not depend on block_m or the weight layout
+# (only the tile list does, which is not compared here), so the block_m
+# variants of one case share them.
+_CASE = {}
+
+
+def _case(w, T, seed, afmt, wfmt):
+    key = (id(w), T, seed, afmt, wfmt)
+    if _CASE.get("key") != key:
+        _CASE.clear()
+        torch.cuda.empty_cache()
+        logits = synth.router_logits(w, T, seed)
+        bias = synth.router_bias(w)
+        xb = synth.activations(w, T, seed)
+        rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+        experts = sorted(set(rid.reshape(-1).tolist()) | set(range(w.E, w.E + w.n_shared)))
+        np_w, dev_w = build_weights(w, experts, wfmt, torch_empty_experts=True)
+        ref = OL.moe_layer(xb, logits, bias, np_w, E=w.E, n_shared=w.n_shared,
+                           n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt=afmt,
+                           wfmt=wfmt, block_m=16, topk_ids=rid, topk_w=rw)
+        _CASE.update(key=key, logits=logits, bias=bias, xb=xb, rid=rid, rw=rw, dev_w=dev_w,
+                     ref=ref)
+    return _CASE
+
+
 def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, fragment=True):
-    logits = synth.router_logits(w, T, seed)
-    bias = synth.router_bias(w)
-    xb = synth.activations(w, T, seed)
-    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    experts = sorted(set(rid.reshape(-1).tolist()) | set(range(w.E, w.E + w.n_shared)))
-    np_w, dev_w = build_weights(w, experts, wfmt, torch_empty_experts=True)
+    c = _case(w, T, seed, afmt, wfmt)
+    logits, bias, xb, rid, rw, ref = c["logits"], c["bias"], c["xb"], c["rid"], c["rw"], c["ref"]
     cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                               topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
                               block_m=block_m, fragment_layout=fragment)
-    layer = gpu_lib.MoELayer(cfg, dev_w)
+    layer = gpu_lib.MoELayer(cfg, c["dev_w"])
     b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
-    ref = OL.moe_layer(xb, logits, bias, np_w, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                       topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
-                       block_m=block_m, topk_ids=rid, topk_w=rw)
     assert_equal(host(b["topk_ids"]), rid, "topk_ids")
     np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
     assert_equal(host(b["perm"]["sorted_pairs"]), ref["perm"]["sorted_pairs"], "sorted_pairs")
