@@ -139,6 +139,11 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int 
   FP4MOE_REQUIRE(expert_offsets && n_tiles && n_dropped && (T == 0 || tiles),
                  "moe_permute: null output pointer");
   FP4MOE_REQUIRE(T == 0 || (topk_ids && sorted_pairs && pair_pos), "moe_permute: null pointer");
+  const bool small = P <= kSmallPairs;
+  const size_t need = moe_permute_workspace(T, topk, E, n_shared, block_m);
+  if (!small && (!workspace || workspace_bytes < need))
+    return set_error(FP4MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes",
+                     workspace_bytes, need);
   FP4MOE_CHECK_DEVICE();
   hipStream_t s = as_stream(stream);
   if (P <= kSmallPairs && E + n_shared <= kHistMaxExperts) {
@@ -154,10 +159,6 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int 
                        n_dropped);
     return check_launch("moe_permute");
   }
-  const size_t need = moe_permute_workspace(T, topk, E, n_shared, block_m);
-  if (!workspace || workspace_bytes < need)
-    return set_error(FP4MOE_ERR_WORKSPACE, "moe_permute: workspace %zu < %zu bytes",
-                     workspace_bytes, need);
   const int nblk = (int)((P + kChunk - 1) / kChunk);
   int32_t* ws = static_cast<int32_t*>(workspace);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(256), 0, s, topk_ids, T, topk, E,

@@ -295,14 +295,14 @@ extern "C" int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_cou
   FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)y & 15) == 0 &&
                      ((uintptr_t)y_f16 & 15) == 0 && ((uintptr_t)codes & 3) == 0,
                  "nvfp4_qdq: x, y, y_f16 must be 16-byte and codes 4-byte aligned");
+  if (!tensor_scale_in && (!workspace || workspace_bytes < nvfp4_qdq_workspace()))
+    return set_error(FP4MOE_ERR_WORKSPACE, "nvfp4_qdq: dynamic scale needs %zu bytes",
+                     nvfp4_qdq_workspace());
   FP4MOE_CHECK_DEVICE();
   hipStream_t s = as_stream(stream);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   const int64_t chunks = (int64_t)M * (K / 8);
   if (!tensor_scale_in) {
-    if (!workspace || workspace_bytes < nvfp4_qdq_workspace())
-      return set_error(FP4MOE_ERR_WORKSPACE, "nvfp4_qdq: dynamic scale needs %zu bytes",
-                       nvfp4_qdq_workspace());
     hipLaunchKernelGGL(nvfp4_zero_kernel, dim3(1), dim3(1), 0, s, ws);
     // about 16 chunks per lane, at most 1024 workgroups (atomics)
     int64_t g = (chunks + 256 * 16 - 1) / (256 * 16);

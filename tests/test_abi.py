@@ -184,6 +184,22 @@ def test_linear_rejects_bad_arguments():
     assert run(M=0, layout=1, stride=0)[0] == 0
 
 
+def test_too_small_workspace_is_reported():
+    """The multi-launch permutation and the dynamic NVFP4 scale need caller
+    workspace; too little returns FP4MOE_ERR_WORKSPACE (3) before any launch
+    (the pointers below are never dereferenced)."""
+    fake = ctypes.c_void_p(4096)
+    need = fm.load().moe_permute_workspace(200, 8, 384, 1, 16)
+    assert need > 0
+    for ws, nbytes in ((None, 0), (fake, need - 4)):
+        st, msg = _status(lambda lib: lib.moe_permute(fake, 200, 8, 384, 1, 16, ws, nbytes, fake,
+                                                      fake, fake, fake, fake, fake, None))
+        assert st == 3 and "workspace" in msg
+    st, msg = _status(lambda lib: lib.nvfp4_qdq(fake, 4, 32, None, None, fake, None, None, None,
+                                                 None, None, None, 0, None))
+    assert st == 3 and "nvfp4_qdq" in msg
+
+
 def test_preshuffle_rejects_bad_shapes():
     st, msg = _status(lambda lib: lib.fp4_weight_preshuffle(0, 2, 24, 256, None, None, None,
                                                              None, None))

@@ -155,9 +155,38 @@ def test_layer_prefill_path_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", block_m)
 
 
+
+
+def _twice(gpu_lib, w, T, afmt, wfmt, block_m):
+    """Run the layer twice on the same inputs; every output byte must agree."""
+    c = _case(w, T, 0, afmt, wfmt)
+    cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
+                              block_m=block_m)
+    layer = gpu_lib.MoELayer(cfg, c["dev_w"])
+    runs = []
+    for _ in range(2):
+        b = layer.forward(bf16_dev(c["xb"]), dev(c["logits"]), dev(c["bias"]), keep=True)
+        runs.append({k: host(b[k]).copy() for k in ("topk_ids", "topk_w")} |
+                    {k: bits_of(b[k]).copy() for k in ("h", "y", "out")} |
+                    {k: host(b["perm"][k]).copy() for k in ("sorted_pairs", "pair_pos", "tiles")})
+    for k in runs[0]:
+        assert runs[0][k].tobytes() == runs[1][k].tobytes(), f"{k} differs between two runs"
+
+
+def test_layer_prefill_is_deterministic(gpu_lib):
+    """Wide MXFP4 tiles with the epilogue quantization: no atomics anywhere."""
+    _twice(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", 192)
+
+
 @pytest.mark.parametrize("block_m", [16, 64])
 def test_layer_nvfp4_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", block_m)
+
+
+def test_layer_nvfp4_is_deterministic(gpu_lib):
+    """The NVFP4 tensor amax is an atomic maximum (order-free); the rest has no atomics."""
+    _twice(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", 64)
 
 
 @pytest.mark.parametrize("block_m", [32, 64, 192])
