@@ -90,10 +90,18 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the NVFP4 layer and the FP8 conversion / FP8 layer measurements")
+    ap.add_argument("--extra", default="nvfp4,fp8,dense",
+                    help="comma-separated subset of the extra workloads to measure "
+                         "(nvfp4, fp8, dense)")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.extra = [x.strip() for x in args.extra.split(",") if x.strip()]
+    bad = [x for x in args.extra if x not in ("nvfp4", "fp8", "dense")]
+    if bad:
+        ap.error(f"--extra: unknown workload(s) {bad} (choose from nvfp4, fp8, dense)")
+    return args
 
 
 def log(args, *a):
@@ -563,9 +571,10 @@ def main():
     if not args.no_extra:
         del dev_w
         torch.cuda.empty_cache()
-        extra["nvfp4"] = run_nvfp4(fm, 10, torch, args)
-        extra["fp8"] = run_fp8(fm, 3, torch, args)
-        extra["dense"] = run_dense(fm, 10, torch, args)
+        runs = {"nvfp4": (run_nvfp4, 10), "fp8": (run_fp8, 3), "dense": (run_dense, 10)}
+        for name in args.extra:
+            fn, steps = runs[name]
+            extra[name] = fn(fm, steps, torch, args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args)

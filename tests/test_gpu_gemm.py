@@ -373,9 +373,11 @@ def test_preshuffle_layout(gpu_lib, wfmt):
 
 LINEAR_CASES = [
     # M, N, K, a_layout, seed: single rows, ragged 192-row tails, several column
-    # blocks, both activation layouts, the hidden width as K
+    # blocks, both activation layouts, the hidden width as K; the last two have
+    # more row tiles than one group of the work order (8) and a short last group
     (1, 512, 128, 0, 81), (37, 512, 256, 1, 82), (192, 1024, 512, 0, 83),
     (500, 1536, 1024, 1, 84), (2000, 512, 7168, 0, 85), (385, 2048, 2048, 1, 86),
+    (2000, 1536, 256, 1, 87), (3100, 2560, 384, 0, 88),
 ]
 
 
