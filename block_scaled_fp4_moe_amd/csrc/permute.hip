@@ -70,32 +70,40 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   __shared__ int tmp[1024];
   const int k = topk + n_shared, P = T * k, Et = E + n_shared;
   // Per expert: exclusive scan over the chunks (in place), total into cnt.
+  // The counts are loaded kScanBatch at a time, so that one memory round trip
+  // serves kScanBatch chunks instead of one.
+  constexpr int kScanBatch = 16;
   for (int e = threadIdx.x; e < Et; e += blockDim.x) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = ws[(int64_t)b * Et + e];
-      ws[(int64_t)b * Et + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j)
+        c[j] = (b0 + j < nblk) ? ws[(int64_t)(b0 + j) * Et + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < nblk) ws[(int64_t)(b0 + j) * Et + e] = run;
+        run += c[j];
+      }
     }
     cnt[e] = run;
   }
   __syncthreads();
+  // expert_offsets receives each expert's first sorted position; the scatter
+  // adds it to the chunk prefixes left in ws
   finish_offsets(cnt, tcnt, tmp, Et, P, block_m, expert_offsets, tiles, n_tiles, n_dropped,
                  sorted_pairs);
-  for (int e = threadIdx.x; e < Et; e += blockDim.x) {
-    const int off = cnt[e];
-    for (int b = 0; b < nblk; ++b) ws[(int64_t)b * Et + e] += off;
-  }
 }
 
 __global__ __launch_bounds__(64) void permute_scatter_kernel(
     const int32_t* __restrict__ ids, int T, int topk, int E, int n_shared,
-    const int32_t* __restrict__ ws, int32_t* __restrict__ sorted_pairs,
-    int32_t* __restrict__ pair_pos) {
+    const int32_t* __restrict__ ws, const int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_pos) {
   __shared__ int cur[kMaxExperts];
   const int k = topk + n_shared, P = T * k, Et = E + n_shared;
+  // cursor = expert's first sorted position + pairs of the expert in earlier chunks
   const int32_t* base = ws + (int64_t)blockIdx.x * Et;
-  for (int e = threadIdx.x; e < Et; e += 64) cur[e] = base[e];
+  for (int e = threadIdx.x; e < Et; e += 64) cur[e] = expert_offsets[e] + base[e];
   __syncthreads();
   const int p0 = blockIdx.x * kChunk, p1 = min(P, p0 + kChunk);
   for (int g = p0; g < p1; g += 64) {
@@ -166,6 +174,6 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int 
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, nblk, T, topk, E, n_shared,
                      block_m, ws, expert_offsets, sorted_pairs, tiles, n_tiles, n_dropped);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(64), 0, s, topk_ids, T, topk, E,
-                     n_shared, ws, sorted_pairs, pair_pos);
+                     n_shared, ws, expert_offsets, sorted_pairs, pair_pos);
   return check_launch("moe_permute");
 }

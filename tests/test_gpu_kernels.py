@@ -114,7 +114,8 @@ def _perm_check(gpu_lib, ids, E, n_shared, bm):
     (20, 8, 2000, 1, 16, 10),           # more experts than the histogram form holds
     (114, 8, 384, 1, 16, 5),            # 1026 pairs: three-kernel path
     (3000, 8, 384, 1, 64, 6), (2048, 8, 384, 0, 256, 7), (16, 2, 8, 0, 16, 8),
-    (500, 4, 4000, 2, 32, 9)])
+    (500, 4, 4000, 2, 32, 9),
+    (5000, 8, 384, 1, 16, 13), (8192, 8, 384, 1, 192, 12)])   # 44 / 72 chunks: batched chunk scan
 def test_permute_parity(gpu_lib, T, topk, E, ns, bm, seed):
     g = np.random.default_rng(seed)
     ids = np.stack([g.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
