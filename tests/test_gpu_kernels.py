@@ -208,7 +208,7 @@ def _quant_inputs(seed, M, K):
     return xb
 
 
-@pytest.mark.parametrize("M,K", [(16, 256), (37, 7168), (300, 2048)])
+@pytest.mark.parametrize("M,K", [(16, 256), (37, 7168), (300, 2048), (9, 800), (6, 96)])
 def test_mxfp4_quant_parity(gpu_lib, M, K):
     xb = _quant_inputs(M + K, M, K)
     codes, scales = gpu_lib.mxfp4_quant_1x32(bf16_dev(xb))
@@ -255,7 +255,7 @@ def test_mxfp4_quant_every_finite_bf16(gpu_lib):
         assert_equal(host(codes), rc, "codes")
 
 
-@pytest.mark.parametrize("M,K", [(8, 128), (37, 512), (64, 7168)])
+@pytest.mark.parametrize("M,K", [(8, 128), (37, 512), (64, 7168), (5, 640)])
 def test_mxfp4_quant_chunked_parity(gpu_lib, M, K):
     xb = _quant_inputs(M * 3 + K, M, K)
     codes, scales = gpu_lib.mxfp4_quant_1x32_chunked(bf16_dev(xb))
