@@ -9,22 +9,23 @@ namespace fp4moe {
 // dispatch
 // ===========================================================================
 
-static int g_num_cus = 0;
+// compute-unit count per device ordinal, read once (0 = not read yet); a
+// racing first read stores the same value
+static int g_num_cus[64] = {};
 
 int grid_cap() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    (void)hipGetDevice(&dev);
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  int n = (dev >= 0 && dev < 64) ? g_num_cus[dev] : 0;
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    g_num_cus = n;
+    if (dev >= 0 && dev < 64) g_num_cus[dev] = n;
   }
-  return g_num_cus * 8;
+  return n * 8;
 }
 
 }  // namespace fp4moe
-
-using namespace fp4moe;
 
 using namespace fp4moe;
 
