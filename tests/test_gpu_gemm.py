@@ -16,7 +16,7 @@ from oracle import gemm as OG
 from oracle import permute as OP
 from oracle import quant as OQ
 
-from .parity import assert_bf16_close, assert_float_close
+from .parity import assert_bf16_close, assert_equal, assert_float_close
 from .test_gpu_kernels import bf16_dev, bits_of, chunk_major, dev, host
 
 pytestmark = pytest.mark.gpu
@@ -422,3 +422,29 @@ def test_mxfp4_linear_exact_special_case(gpu_lib):
     gpu_lib.mxfp4_linear(dev(qc), dev(qs), fc[0], fs[0], out_f32=out_f32)
     ref = F.mxfp4_dequant(qc, qs) @ OG.dequant_expert("mx", codes[0], scale[0]).T
     assert np.array_equal(host(out_f32).astype(np.float64), ref)
+
+
+def test_mxfp4_linear_full_size_sampled(gpu_lib):
+    """The dense linear at the benchmarked size and launch configuration (M=16384,
+    N=K=7168, activations quantized chunk-major on the device, 192 x 512 tiles):
+    the activation codes and the outputs of sampled rows (first and last rows,
+    both sides of a 192-row tile boundary, random rows) against the oracle."""
+    M, N, K = 16384, 7168, 7168
+    rng = np.random.default_rng(91)
+    xb = synth.bf16_from_f32(rng.standard_normal((M, K), dtype=np.float32))
+    wd = make_weights(rng, 1, N, K, "mx")
+    fc, fs = gpu_lib.fp4_weight_preshuffle(gpu_lib.WFMT["mx"], dev(wd["codes"]), dev(wd["scale"]))
+    codes, scales = gpu_lib.mxfp4_quant_1x32_chunked(bf16_dev(xb))
+    out_f32 = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    out = gpu_lib.mxfp4_linear(codes, scales, fc[0], fs[0], a_layout=1, M=M, out_f32=out_f32)
+    rows = np.unique(np.concatenate([[0, 191, 192, 8191, 8192, M - 1],
+                                     rng.choice(M, 10, replace=False)]))
+    qc, qs = OQ.mxfp4_quant_1x32(xb[rows])
+    hc, hs = host(codes), host(scales)                 # [K/128, M, 64], [K/128, M, 4]
+    assert_equal(np.ascontiguousarray(hc[:, rows].transpose(1, 0, 2)).reshape(len(rows), K // 2),
+                 qc, "sampled activation codes")
+    assert_equal(np.ascontiguousarray(hs[:, rows].transpose(1, 0, 2)).reshape(len(rows), K // 32),
+                 qs, "sampled activation scales")
+    ref = F.mxfp4_dequant(qc, qs) @ oracle_weight(wd, "mx", 0).T
+    assert_float_close(host(out_f32)[rows], ref, "full-size mxfp4_linear f32 (sampled rows)")
+    assert_bf16_close(bits_of(out)[rows], ref, "full-size mxfp4_linear bf16 (sampled rows)")

@@ -399,6 +399,28 @@ def test_convert_parity(gpu_lib, R, K, lo, hi, seed):
     _convert_check(gpu_lib, codes, scales)
 
 
+def test_convert_full_size_sampled(gpu_lib):
+    """The conversion at the benchmarked size (the gate/up weights of all 385
+    experts, 1576960 rows x 7168, row scale spans U{1..9} binades): every row
+    exact (status 0, no inexact row: the span <= 9 invariant at full size), and
+    sampled rows bit-exact against the oracle."""
+    w = synth.WORKLOADS["skewed"]
+    R, K = (w.E + w.n_shared) * 2 * w.I, w.H
+    g = np.random.default_rng(99)
+    codes = g.integers(0, 256, (R, K // 2), dtype=np.uint8)
+    scales, _ = synth.spanned_scales(R, K // 32, 5, 99, top_lo=-4, top_hi=0, span_lo=1, span_hi=9)
+    fp8, sc, st, ni = gpu_lib.mxfp4_to_fp8_channel(dev(codes), dev(scales))
+    assert int(host(ni)[0]) == 0
+    assert not np.any(host(st))
+    rows = np.unique(np.concatenate([[0, 1, R // 2, R - 1], g.choice(R, 60, replace=False)]))
+    ref = OC.mxfp4_to_fp8_channel(codes[rows], scales[rows])
+    assert_equal(host(fp8[rows]), ref["fp8"], "fp8 codes (sampled rows)")
+    assert_equal(host(sc[rows]), ref["scale"], "channel scale (sampled rows)")
+    assert_equal(host(st[rows]), ref["status"], "row status (sampled rows)")
+    del fp8, sc, st
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ combine
 
 @pytest.mark.parametrize("T,topk,ns,H", [(1, 8, 1, 7168), (37, 2, 0, 256), (300, 8, 1, 2048)])

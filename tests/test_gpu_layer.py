@@ -157,6 +157,185 @@ def test_layer_prefill_path_full_width(gpu_lib, block_m):
 
 
 
+def test_layer_prefill_full_size_sampled(gpu_lib):
+    """The prefill layer at the benchmarked size and launch configuration
+    (T=8192, uniform routing, MXFP4 activations, 192-row tiles with h quantized
+    in the stage-1 epilogue, no intermediate copies kept): routing ids and the
+    permutation of every token bit-exact, and the outputs of sampled tokens
+    against the oracle layer run on those tokens alone (a token's output
+    depends only on its own row, its routing and the weights)."""
+    from oracle import permute as OP
+    w = synth.WORKLOADS["prefill"]
+    T, Et = w.T, w.E + w.n_shared
+    logits = synth.router_logits(w, T, 0)
+    bias = synth.router_bias(w)
+    xb = synth.activations(w, T, 0)
+    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+    sub = np.array([0, T // 2 + 3, T - 1])
+    need = set(rid[sub].reshape(-1).tolist()) | set(range(w.E, Et))
+    H, I = w.H, w.I
+    dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
+                 w13_scale=torch.empty((Et, 2 * I, H // 32), dtype=torch.uint8, device="cuda"),
+                 w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
+                 w2_scale=torch.empty((Et, H, I // 32), dtype=torch.uint8, device="cuda"))
+    np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+    for e in range(Et):                      # every expert receives tokens at this size
+        for proj, name in ((13, "w13"), (2, "w2")):
+            c, sc = synth.expert_mx(w, e, proj)
+            dev_w[name][e].copy_(torch.from_numpy(c))
+            dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
+            if e in need:
+                np_w[name][e], np_w[name + "_scale"][e] = c, sc
+    cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt="mx",
+                              block_m=192)
+    layer = gpu_lib.MoELayer(cfg, dev_w)
+    del dev_w
+    out = layer.forward(bf16_dev(xb), dev(logits), dev(bias))
+    b = layer._bufs[T]
+    assert_equal(host(b["topk_ids"]), rid, "topk_ids")
+    np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
+    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
+    assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
+    assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
+    ref = OL.moe_layer(xb[sub], logits[sub], bias, np_w, E=w.E, n_shared=w.n_shared,
+                       n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
+                       wfmt="mx", block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
+    assert_bf16_close(bits_of(out)[sub], ref["out"], "out (sampled tokens)")
+    del layer
+    torch.cuda.empty_cache()
+
+
+def test_layer_fp8_full_size_sampled(gpu_lib):
+    """The FP8-weight layer at the benchmarked size and launch configuration
+    (T=16384, Zipf(1.1) routing, MXFP4 activations x E4M3 weights with
+    power-of-two channel scales on the 192-row scaled-MFMA tiles): routing and
+    permutation of every token bit-exact, sampled token outputs against the
+    oracle layer run on those tokens alone.  The E4M3 codes are uniform bytes
+    without the NaN patterns (any E4M3 operand exercises the same arithmetic as
+    the converted experts)."""
+    from oracle import permute as OP
+    w = synth.WORKLOADS["skewed"]
+    T, Et, H, I = w.T, w.E + w.n_shared, w.H, w.I
+    logits = synth.router_logits(w, T, 0)
+    bias = synth.router_bias(w)
+    xb = synth.activations(w, T, 0)
+    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+    sub = np.array([0, T // 3, T - 1])
+    need = set(rid[sub].reshape(-1).tolist()) | set(range(w.E, Et))
+    dev_w = dict(w13=torch.empty((Et, 2 * I, H), dtype=torch.uint8, device="cuda"),
+                 w13_scale=torch.empty((Et, 2 * I), dtype=torch.float32, device="cuda"),
+                 w2=torch.empty((Et, H, I), dtype=torch.uint8, device="cuda"),
+                 w2_scale=torch.empty((Et, H), dtype=torch.float32, device="cuda"))
+    np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+    g = np.random.default_rng(97)
+    for e in range(Et):
+        for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+            c = g.integers(0, 256, (N, K), dtype=np.uint8)
+            c[(c & 0x7F) == 0x7F] = 0x3C
+            sc = np.ldexp(1.0, g.integers(-9, -3, N)).astype(np.float32)
+            dev_w[name][e].copy_(torch.from_numpy(c))
+            dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
+            if e in need:
+                np_w[name][e], np_w[name + "_scale"][e] = c, sc
+    cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt="fp8",
+                              block_m=192)
+    layer = gpu_lib.MoELayer(cfg, dev_w)
+    del dev_w
+    out = layer.forward(bf16_dev(xb), dev(logits), dev(bias))
+    b = layer._bufs[T]
+    assert_equal(host(b["topk_ids"]), rid, "topk_ids")
+    np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
+    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
+    assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
+    assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
+    ref = OL.moe_layer(xb[sub], logits[sub], bias, np_w, E=w.E, n_shared=w.n_shared,
+                       n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
+                       wfmt="fp8", block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
+    assert_bf16_close(bits_of(out)[sub], ref["out"], "out (sampled tokens)")
+    del layer
+    torch.cuda.empty_cache()
+
+
+def test_layer_nvfp4_full_size_sampled(gpu_lib):
+    """The NVFP4 emulation layer at the benchmarked size and launch configuration
+    (T=2048, 64-row tiles, activations in the f16 operand form): routing and
+    permutation of every token bit-exact, the activation QDQ of every token
+    bit-exact, and sampled rows of h against the oracle's stage 1.  The second
+    QDQ takes one tensor scale over all of h, which couples every token, so the
+    final outputs are checked at full width on fewer tokens instead
+    (test_layer_nvfp4_full_width).  Weights: uniform code bytes, positive
+    finite E4M3 block scales, tensor scales U(0.01, 0.02)."""
+    from oracle import formats as F
+    from oracle import gemm as OG
+    from oracle import permute as OP
+    from oracle import quant as OQ
+    w = synth.WORKLOADS["nvfp4"]
+    T, Et, H, I = w.T, w.E + w.n_shared, w.H, w.I
+    k = w.topk + w.n_shared
+    logits = synth.router_logits(w, T, 0)
+    bias = synth.router_bias(w)
+    xb = synth.activations(w, T, 0)
+    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
+    perm = OP.moe_permute(rid, w.E, w.n_shared, 64)
+    offs = perm["expert_offsets"]
+    counts = np.diff(offs)
+    # sampled sorted rows: first and last row of the most loaded expert, of a
+    # one-row expert if any, and random rows
+    g = np.random.default_rng(98)
+    big = int(np.argmax(counts))
+    rows = [offs[big], offs[big + 1] - 1]
+    single = np.flatnonzero(counts == 1)
+    if single.size:
+        rows.append(offs[single[0]])
+    rows = np.unique(np.concatenate([rows, g.choice(int(offs[-1]), 9, replace=False)]))
+    row_e = np.searchsorted(offs, rows, side="right") - 1
+    dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
+                 w13_scale=torch.empty((Et, 2 * I, H // 16), dtype=torch.uint8, device="cuda"),
+                 w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
+                 w2_scale=torch.empty((Et, H, I // 16), dtype=torch.uint8, device="cuda"))
+    ts = {"w13": g.uniform(0.01, 0.02, Et).astype(np.float32),
+          "w2": g.uniform(0.01, 0.02, Et).astype(np.float32)}
+    w13 = {}
+    sampled_experts = set(row_e.tolist())
+    for e in range(Et):
+        for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+            c = g.integers(0, 256, (N, K // 2), dtype=np.uint8)
+            sc = g.integers(0x01, 0x7F, (N, K // 16), dtype=np.uint8)   # positive finite E4M3
+            dev_w[name][e].copy_(torch.from_numpy(c))
+            dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
+            if name == "w13" and e in sampled_experts:
+                w13[e] = (c, sc)
+    dev_w["w13_ts"], dev_w["w2_ts"] = dev(ts["w13"]), dev(ts["w2"])
+    cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt="nvfp4", wfmt="nvfp4",
+                              block_m=64)
+    layer = gpu_lib.MoELayer(cfg, dev_w)
+    del dev_w
+    b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
+    assert_equal(host(b["topk_ids"]), rid, "topk_ids")
+    np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
+    assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
+    assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
+    # activation QDQ of every token: the f16 operand times its power-of-two scale
+    qx = OQ.nvfp4_qdq(xb)
+    y_ref = F.bf16_decode(qx["y"])
+    y_gpu = host(b["xq"]).astype(np.float64) * float(host(b["xs"])[0])
+    assert np.array_equal(y_gpu, y_ref), "activation QDQ (f16 form)"
+    # stage 1 on sampled sorted rows
+    tok = perm["sorted_pairs"][rows] // k
+    h_gpu = bits_of(b["h"])[rows]
+    ref = np.empty((len(rows), I))
+    for i, (r, e) in enumerate(zip(rows, row_e)):
+        c, sc = w13[int(e)]
+        wd = OG.dequant_expert("nvfp4", c, sc, ts["w13"][e])
+        ref[i] = OG.stage1_expert(y_ref[tok[i]][None, :], wd)[0]
+    assert_bf16_close(h_gpu, ref, "h (sampled rows)")
+    del layer, b
+    torch.cuda.empty_cache()
+
+
 def _twice(gpu_lib, w, T, afmt, wfmt, block_m):
     """Run the layer twice on the same inputs; every output byte must agree."""
     c = _case(w, T, 0, afmt, wfmt)
