@@ -96,7 +96,8 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                       (a->block_m == 128 || a->block_m == 192 || a->block_m == 256)),
                  "fp4_grouped_gemm: chunked activations need MXFP4 activations, fragment "
                  "weights and block_m 128, 192 or 256 (FP8 weights: 192)");
-  FP4MOE_REQUIRE(!a_chunked || (a->a_rows >= 1 && a->a_rows <= (1 << 26) &&
+  // (an empty batch, max_rows 0, may come with an empty activation slab)
+  FP4MOE_REQUIRE(!a_chunked || (a->a_rows >= (a->max_rows > 0 ? 1 : 0) && a->a_rows <= (1 << 26) &&
                                 (a->a_row_gather || a->a_rows >= a->max_rows)),
                  "fp4_grouped_gemm: a_rows=%d (max_rows=%d)", a->a_rows, a->max_rows);
   // the LDS-DMA tiles (MXFP4 x MXFP4, fragment weights, block_m >= 128) address

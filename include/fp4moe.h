@@ -226,7 +226,9 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * a_layout FP4MOE_A_LAYOUT_CHUNKED (codes and scales of a_rows rows in the
  * layout of mxfp4_quant_1x32_chunked; lda unused) is taken by (MXFP4,
  * MXFP4) with fragment-major weights and block_m 128, 192 or 256; other
- * combinations return FP4MOE_ERR_INVALID_ARG.
+ * combinations return FP4MOE_ERR_INVALID_ARG.  a_rows is in [1, 2^26] and
+ * at least max_rows without a row gather; an empty batch (max_rows 0) may
+ * pass a_rows 0.
  * out_q / out_q_scale (stage 1, block_m 192, MXFP4 activations, out_f32 NULL):
  * the stage-1 output h is also written quantized exactly as
  * mxfp4_quant_1x32_chunked(bf16 h, out_rows = out_q_rows) writes it -- the

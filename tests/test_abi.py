@@ -138,6 +138,8 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**{**wide, "N": 256}, stage=2, max_tiles=0)[0] == 1
     assert run(**wide, stage=2, max_tiles=0)[0] == 0
     assert run(**wide, a_layout=1, a_rows=8, max_tiles=0)[0] == 0
+    assert run(**wide, a_layout=1, a_rows=0, max_rows=0, max_tiles=0)[0] == 0   # empty batch
+    assert run(**wide, a_layout=1, a_rows=0, max_tiles=0)[0] == 1               # rows but no slab
     assert run(**{**wide, "block_m": 160})[0] == 1
     assert run(**{**wide, "ldo": 516}, max_tiles=0)[0] == 1     # 16-byte row stores
     # FP8 weights x MXFP4 activations at block_m 192 (192 x 256 tiles)

@@ -145,6 +145,32 @@ def test_layer_tiny_mx_path(gpu_lib):
     run_layer(gpu_lib, synth.WORKLOADS["tiny"], 16, "mx", "mx", 32)
 
 
+@pytest.mark.parametrize("afmt,block_m", [("bf16", 16), ("mx", 32), ("mx", 192)])
+def test_layer_empty_batch(gpu_lib, afmt, block_m):
+    """T = 0: every call accepts the empty batch and the layer returns an empty
+    output (the one-launch routing + permutation at decode sizes, the separate
+    calls otherwise)."""
+    w = synth.WORKLOADS["tiny"]
+    # the 192-row tiles need output widths in whole 256 / 512-column blocks
+    H, I = (512, 256) if block_m == 192 else (w.H, w.I)
+    cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt="mx",
+                              block_m=block_m)
+    Et = w.E + w.n_shared
+    g = np.random.default_rng(5)
+    wts = {}
+    for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+        wts[name] = dev(g.integers(0, 256, (Et, N, K // 2), dtype=np.uint8))
+        wts[name + "_scale"] = dev(np.full((Et, N, K // 32), 127, np.uint8))
+    layer = gpu_lib.MoELayer(cfg, wts)
+    x = torch.zeros((0, H), dtype=torch.bfloat16, device="cuda")
+    logits = torch.zeros((0, w.E), dtype=torch.float32, device="cuda")
+    bias = torch.zeros(w.E, dtype=torch.float32, device="cuda")
+    out = layer.forward(x, logits, bias)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (0, H)
+
+
 @pytest.mark.parametrize("T", [1, 8])
 def test_layer_decode_full_width(gpu_lib, T):
     run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
