@@ -186,6 +186,13 @@ def test_linear_rejects_bad_arguments():
     assert run(M=0, layout=1, stride=0)[0] == 0
 
 
+def test_combine_rejects_too_many_tokens():
+    fake = ctypes.c_void_p(4096)
+    st, msg = _status(lambda lib: lib.moe_combine(fake, fake, fake, 65536, 8, 1, 64, fake, None,
+                                                   None))
+    assert st == 1 and "65535" in msg
+
+
 def test_too_small_workspace_is_reported():
     """The multi-launch permutation and the dynamic NVFP4 scale need caller
     workspace; too little returns FP4MOE_ERR_WORKSPACE (3) before any launch

@@ -423,7 +423,8 @@ def test_convert_full_size_sampled(gpu_lib):
 
 # ------------------------------------------------------------------ combine
 
-@pytest.mark.parametrize("T,topk,ns,H", [(1, 8, 1, 7168), (37, 2, 0, 256), (300, 8, 1, 2048)])
+@pytest.mark.parametrize("T,topk,ns,H", [(1, 8, 1, 7168), (37, 2, 0, 256), (300, 8, 1, 2048),
+                                         (65535, 8, 1, 64)])   # the largest T (one grid row per token)
 def test_combine_parity(gpu_lib, T, topk, ns, H):
     g = np.random.default_rng(T * H)
     k = topk + ns
