@@ -176,6 +176,12 @@ def test_layer_decode_full_width(gpu_lib, T):
     run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
 
 
+def test_layer_decode_is_deterministic(gpu_lib):
+    """The decode path (one-launch routing + permutation, split-K reduction in
+    LDS in a fixed order): every output byte the same on a second run."""
+    _twice(gpu_lib, synth.WORKLOADS["decode"], 8, "bf16", "mx", 16)
+
+
 @pytest.mark.parametrize("block_m", [64, 192, 256])
 def test_layer_prefill_path_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", block_m)
@@ -397,6 +403,11 @@ def test_layer_nvfp4_is_deterministic(gpu_lib):
 @pytest.mark.parametrize("block_m", [32, 64, 192])
 def test_layer_fp8_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", block_m)
+
+
+def test_layer_fp8_is_deterministic(gpu_lib):
+    """FP4 x FP8 192-row tiles: no atomics anywhere."""
+    _twice(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", 192)
 
 
 @pytest.mark.parametrize("T", [8, 64])
