@@ -39,6 +39,22 @@ def activation_values(afmt, x_bits):
     raise ValueError(afmt)
 
 
+def stage2_activation(afmt, h, h_bits, rounding=True):
+    """The values stage 2 sees for the stage-1 output of the sorted rows.
+
+    h is rounded to bf16 (h_bits) and then takes the same activation path as x
+    ([ATOM] "Stage B: Dynamic Activation Quantization": each GEMM's live
+    activations are quantized at run time; [NVFP4] "Weight Dequantization and
+    Activation QDQ": a QDQ round trip before each GEMM).  For NVFP4 the
+    dynamic tensor scale is taken over all sorted rows [0, n_rows) of h at
+    once, as over all tokens of x before stage 1.  With rounding off the
+    unrounded h passes straight through.
+    """
+    if not rounding:
+        return h
+    return activation_values(afmt, h_bits)
+
+
 def weight_getter(wfmt, weights, name):
     def get(e):
         if wfmt == "nvfp4":
@@ -64,7 +80,7 @@ def moe_layer(x_bits, logits, bias, weights, *, E, n_shared, n_group, topk_group
     h = G.grouped_stage(1, a1, perm["expert_offsets"], weight_getter(wfmt, weights, "w13"),
                         rounding)
     h_bits = F.bf16_bits(h)
-    a2 = activation_values(afmt, h_bits) if rounding else h
+    a2 = stage2_activation(afmt, h, h_bits, rounding)
     y = G.grouped_stage(2, a2, perm["expert_offsets"], weight_getter(wfmt, weights, "w2"),
                         rounding)
     y_bits = F.bf16_bits(y)

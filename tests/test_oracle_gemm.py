@@ -134,3 +134,95 @@ def test_nvfp4_and_fp8_dequant_paths():
     cs = np.array([0.5, 2.0 ** -20, 8.0], dtype=np.float32)
     w = G.dequant_expert("fp8", f8, cs)
     assert np.array_equal(w, F.e4m3_decode(f8) * cs[:, None].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# The activation chaining of the layer (afmt "mx" and "nvfp4"), pinned by a
+# per-token, per-slot brute force that uses no permutation, no grouped stage
+# and no sorted-row order.  [ATOM] "Stage B: Dynamic Activation Quantization":
+# the live activations of each GEMM are quantized at run time, so h is
+# re-quantized before stage 2.  [NVFP4] "Weight Dequantization and Activation
+# QDQ": a QDQ round trip before each GEMM; the dynamic tensor scale of stage 2
+# covers every (token, slot) row of h at once.
+# --------------------------------------------------------------------------
+
+def _chain_weights(wfmt, Et, H, I, seed):
+    g = np.random.default_rng(seed)
+    if wfmt == "mx":
+        return _tiny_weights(Et, H, I, seed)
+    w = {}
+    for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+        w[name] = g.integers(0, 256, (Et, N, K // 2), dtype=np.uint8)
+        w[name + "_scale"] = synth.e4m3_from_f32(
+            np.abs(g.standard_normal((Et, N, K // 16))).astype(np.float32))
+        w[name + "_ts"] = g.uniform(0.01, 0.02, Et).astype(np.float32)
+    return w
+
+
+def _chain_brute_force(xb, ids, wts, w, afmt, wfmt, E, n_shared, I, requant_h=True):
+    """out float64 [T, H] of the layer, one token and one slot at a time."""
+    from oracle import quant as Q
+    T = xb.shape[0]
+    topk = ids.shape[1]
+
+    def weight(name, e):
+        if wfmt == "mx":
+            return F.mxfp4_dequant(w[name][e], w[name + "_scale"][e])
+        return F.nvfp4_dequant(w[name][e], w[name + "_scale"][e], w[name + "_ts"][e])
+
+    def qdq_rows(rows_bits, s_t=None):
+        if afmt == "mx":
+            return [Q.mxfp4_qdq_values(r[None])[0] for r in rows_bits]
+        return [F.bf16_decode(Q.nvfp4_qdq(r[None], tensor_scale_in=s_t)["y"])[0]
+                for r in rows_bits]
+
+    # stage-1 input: each token alone, the NVFP4 tensor scale over all of x
+    s1 = Q.nvfp4_qdq(xb)["tensor_scale"] if afmt == "nvfp4" else None
+    a = qdq_rows(list(xb), s1)
+    slots = [(t, j, int(ids[t, j]) if j < topk else E + (j - topk))
+             for t in range(T) for j in range(topk + n_shared)]
+    h_bits = []
+    for t, j, e in slots:
+        w13 = weight("w13", e)
+        gate = np.array([sum(w13[n, q] * a[t][q] for q in range(w13.shape[1]))
+                         for n in range(I)])
+        up = np.array([sum(w13[I + n, q] * a[t][q] for q in range(w13.shape[1]))
+                       for n in range(I)])
+        h_bits.append(F.bf16_bits(gate / (1.0 + np.exp(-gate)) * up))
+    if not requant_h:
+        a2 = [F.bf16_decode(hb) for hb in h_bits]
+    else:
+        # the NVFP4 stage-2 tensor scale spans every row of h
+        s2 = Q.nvfp4_qdq(np.stack(h_bits))["tensor_scale"] if afmt == "nvfp4" else None
+        a2 = qdq_rows(h_bits, s2)
+    out = np.zeros((T, xb.shape[1]))
+    for (t, j, e), hv in zip(slots, a2):
+        y = F.bf16_round(weight("w2", e) @ hv)
+        out[t] += (wts[t, j] if j < topk else 1.0) * y
+    return out
+
+
+def _check_chain(afmt, wfmt, seed):
+    g = np.random.default_rng(seed)
+    T, H, I, E, n_shared, topk = 5, 64, 32, 6, 1, 2
+    xb = synth.bf16_from_f32(g.standard_normal((T, H)).astype(np.float32))
+    logits = g.standard_normal((T, E)).astype(np.float32)
+    bias = (g.standard_normal(E) * 0.1).astype(np.float32)
+    w = _chain_weights(wfmt, E + n_shared, H, I, seed + 1)
+    r = L.moe_layer(xb, logits, bias, w, E=E, n_shared=n_shared, n_group=1, topk_group=1,
+                    topk=topk, afmt=afmt, wfmt=wfmt)
+    want = _chain_brute_force(xb, r["topk_ids"], r["topk_w"], w, afmt, wfmt, E, n_shared, I)
+    scale = np.abs(want).max()
+    assert np.allclose(r["out"], want, rtol=1e-12, atol=1e-12 * scale)
+    # the re-quantization of h is visible at this size: without it the layer differs
+    plain = _chain_brute_force(xb, r["topk_ids"], r["topk_w"], w, afmt, wfmt, E, n_shared, I,
+                               requant_h=False)
+    assert np.abs(plain - want).max() > 1e-3 * scale
+
+
+def test_layer_mx_activation_chain_brute_force():
+    _check_chain("mx", "mx", 40)
+
+
+def test_layer_nvfp4_activation_chain_brute_force():
+    _check_chain("nvfp4", "nvfp4", 42)

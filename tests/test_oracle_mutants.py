@@ -14,6 +14,7 @@ import pytest
 import oracle.convert as OC
 import oracle.formats as OF
 import oracle.gemm as OG
+import oracle.layer as OL
 import oracle.quant as OQ
 import oracle.route as OR
 
@@ -25,6 +26,13 @@ _orig_e2m1 = OF.e2m1_decode
 _orig_floor = OF.floor_log2
 _orig_round = OF.round_to_grid
 _orig_silu = OG.silu_mul
+_orig_act = OL.activation_values
+
+
+def _nvfp4_scale_per_row(afmt, x_bits):
+    if afmt != "nvfp4" or x_bits.shape[0] == 0:
+        return _orig_act(afmt, x_bits)
+    return np.concatenate([_orig_act(afmt, x_bits[r:r + 1]) for r in range(x_bits.shape[0])])
 
 
 def _swap_nibbles(packed):
@@ -63,6 +71,10 @@ MUTANTS = {
     "RNE ties away from zero": [(OF, "round_to_grid", _round_ties_away)],
     "MX scale uses emax 1": [(OQ, "E2M1_EMAX", 1)],
     "routing ties to higher id": [(OR, "_order_desc", _order_desc_high_first)],
+    "h not re-quantized before stage 2": [(OL, "stage2_activation",
+                                           lambda afmt, h, h_bits, rounding=True:
+                                           OF.bf16_decode(h_bits) if rounding else h)],
+    "NVFP4 tensor scale per row": [(OL, "activation_values", _nvfp4_scale_per_row)],
     "gate/up swapped": [(OG, "silu_mul", lambda gu, I: _orig_silu(
         np.concatenate([gu[:, I:], gu[:, :I]], axis=1), I))],
 }
