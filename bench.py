@@ -302,6 +302,39 @@ def run_prefill(fm, dev_w, steps, torch, args):
     return r
 
 
+def run_skewed_mx(fm, dev_w, steps, torch, args):
+    """Skewed-routing prefill: T=16384, expert popularity Zipf(1.1) over 384
+    experts (Gumbel-top-k logits), MXFP4 activations x MXFP4 weights on the
+    scaled FP4 MFMA, 192-row tiles (the prefill kernels)."""
+    import synth
+    w = synth.WORKLOADS["skewed"]
+    cfg = fm.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                         topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt="mx", block_m=192)
+    layer = fm.MoELayer(cfg, dev_w, preshuffled=True)
+    bias = torch.from_numpy(synth.router_bias(w)).cuda()
+    batches = [batch_inputs(w, w.T, 5000, torch)]
+    r = time_layer(layer, batches, bias, steps, 2, torch)
+    pairs = w.T * (w.topk + w.n_shared)
+    tflops = FLOP_PER_PAIR * pairs / (r["ms_per_step"] * 1e-3) / 1e12
+    offs = layer._bufs[w.T]["perm"]["expert_offsets"].cpu().numpy()
+    counts = np.diff(offs)[:w.E]
+    log(args, f"skewed mx prefill T={w.T}: {r['ms_per_step']:.3f} ms/step, {tflops:.0f} TFLOP/s, "
+              f"rows per routed expert max {counts.max()} median {int(np.median(counts))} "
+              f"min {counts.min()}, kernels(ms)="
+              + json.dumps({k2: round(v, 3) for k2, v in r['per_kernel_ms'].items()}))
+    del layer
+    torch.cuda.empty_cache()
+    return dict(tflops=round(tflops, 1), ms_per_step=round(r["ms_per_step"], 3),
+                frac=round(tflops / MXFP4_PEAK_TFLOPS, 4),
+                kernels_ms={k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
+                rows_per_routed_expert=dict(max=int(counts.max()), median=float(np.median(counts)),
+                                            min=int(counts.min()),
+                                            empty=int(np.count_nonzero(counts == 0))),
+                workload=f"skewed prefill MoE layer, T={w.T}, Zipf(1.1) expert popularity over "
+                         f"{w.E} experts + 1 shared, MXFP4 activations (mxfp4_quant_1x32) x "
+                         "MXFP4 weights, gfx950 scaled MFMA, block_m 192")
+
+
 def gpu_nvfp4_weights(w, torch, seed=4):
     """NVFP4 weights of all experts drawn on the GPU (seeded torch generator) with
     the same distributions as synth.expert_nvfp4: uniform E2M1 bytes, E4M3
@@ -323,7 +356,9 @@ def gpu_nvfp4_weights(w, torch, seed=4):
 def gpu_spanned_mx_weights(w, torch, seed=5):
     """MXFP4 weights of all experts drawn on the GPU with the row-scale recipe of
     synth.spanned_scales: top code 127+U{-4..0}, span U{1..9} binades, one block
-    at each end of the span, the rest uniform in between; codes uniform bytes."""
+    at each end of the span, the rest uniform in between; codes uniform bytes.
+    Every tensor is drawn for all experts at once (a handful of launches per
+    tensor, no per-expert loop)."""
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     Et = w.E + w.n_shared
@@ -331,19 +366,18 @@ def gpu_spanned_mx_weights(w, torch, seed=5):
     for name, (N, K) in (("w13", (2 * w.I, w.H)), ("w2", (w.H, w.I))):
         out[name] = torch.randint(0, 256, (Et, N, K // 2), dtype=torch.uint8, device="cuda",
                                   generator=g)
-        sc = torch.empty((Et, N, K // 32), dtype=torch.uint8, device="cuda")
         nb = K // 32
-        for e in range(Et):
-            top = 127 + torch.randint(-4, 1, (N, 1), device="cuda", generator=g)
-            span = torch.randint(1, 10, (N, 1), device="cuda", generator=g)
-            u = torch.randint(0, 1 << 30, (N, nb), device="cuda", generator=g)
-            s_ = top - u % (span + 1)
-            p0 = torch.randint(0, nb, (N, 1), device="cuda", generator=g)
-            p1 = (p0 + 1 + torch.randint(0, nb - 1, (N, 1), device="cuda", generator=g)) % nb
-            s_.scatter_(1, p0, top)
-            s_.scatter_(1, p1, top - span)
-            sc[e].copy_(s_.to(torch.uint8))
-        out[name + "_scale"] = sc
+        i32 = dict(dtype=torch.int32, device="cuda", generator=g)
+        top = 127 + torch.randint(-4, 1, (Et, N, 1), **i32)
+        span = torch.randint(1, 10, (Et, N, 1), **i32)
+        p0 = torch.randint(0, nb, (Et, N, 1), **i32)
+        p1 = (p0 + 1 + torch.randint(0, nb - 1, (Et, N, 1), **i32)) % nb
+        col = torch.arange(nb, dtype=torch.int32, device="cuda").view(1, 1, nb)
+        s_ = top - torch.randint(0, 1 << 30, (Et, N, nb), **i32) % (span + 1)
+        s_ = torch.where(col == p0, top, s_)
+        s_ = torch.where(col == p1, top - span, s_)
+        out[name + "_scale"] = s_.to(torch.uint8)
+        del top, span, p0, p1, s_
     return out
 
 
@@ -489,33 +523,103 @@ def run_dense(fm, steps, torch, args):
                          "activations x fragment-major MXFP4 weight, 192x512 scaled-MFMA tiles")
 
 
-def cpu_baseline(w, args):
-    """The oracle as it stands, on one step of the T=8 decode workload, timed on the host."""
+def blas_threads():
+    """Threads of the BLAS library NumPy calls (threadpoolctl), or None."""
+    try:
+        import threadpoolctl
+        info = [d for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        return int(info[0]["num_threads"]) if info else None
+    except Exception:
+        return None
+
+
+def _oracle_layer_timed(wl, T, seed, afmt, wfmt, tokens=None):
+    """Time the oracle layer (routing included) on the tokens `tokens` of a seeded
+    batch of T tokens of workload wl; weight generation is not timed.
+    Returns (seconds, pairs, distinct experts read)."""
     import synth
     from oracle import layer as OL
     from oracle import route as OR
-    T = 8
-    logits = synth.router_logits(w, T, 1000)
-    bias = synth.router_bias(w)
-    xb = synth.activations(w, T, 1000)
-    t0 = time.perf_counter()
-    ids, wts = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    experts = sorted(set(ids.reshape(-1).tolist()) | {w.E})
-    np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
+    logits = synth.router_logits(wl, T, seed)
+    bias = synth.router_bias(wl)
+    xb = synth.activations(wl, T, seed)
+    if tokens is not None:
+        logits, xb = logits[tokens], xb[tokens]
+    ids, _ = OR.moe_route(logits, bias, wl.n_group, wl.topk_group, wl.topk)
+    experts = sorted(set(ids.reshape(-1).tolist()) | set(range(wl.E, wl.E + wl.n_shared)))
+    names = ("w13", "w13_scale", "w2", "w2_scale") + (("w13_ts", "w2_ts") if wfmt == "nvfp4"
+                                                      else ())
+    np_w = {k: {} for k in names}
     for e in experts:
-        np_w["w13"][e], np_w["w13_scale"][e] = synth.expert_mx(w, e, 13)
-        np_w["w2"][e], np_w["w2_scale"][e] = synth.expert_mx(w, e, 2)
-    t1 = time.perf_counter()
-    OL.moe_layer(xb, logits, bias, np_w, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                 topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx",
-                 topk_ids=ids, topk_w=wts)
-    t2 = time.perf_counter()
-    secs = t2 - t1
-    nbytes = len(experts) * (BYTES_W13 + BYTES_W2) + 2 * T * w.H * 2 + T * w.E * 4
-    return dict(value=nbytes / secs / 1e9, unit="GB/s", cores=len(os.sched_getaffinity(0)),
+        if wfmt == "nvfp4":
+            np_w["w13"][e], np_w["w13_scale"][e], np_w["w13_ts"][e] = synth.expert_nvfp4(wl, e, 13)
+            np_w["w2"][e], np_w["w2_scale"][e], np_w["w2_ts"][e] = synth.expert_nvfp4(wl, e, 2)
+        else:
+            np_w["w13"][e], np_w["w13_scale"][e] = synth.expert_mx(wl, e, 13)
+            np_w["w2"][e], np_w["w2_scale"][e] = synth.expert_mx(wl, e, 2)
+    t0 = time.perf_counter()
+    OL.moe_layer(xb, logits, bias, np_w, E=wl.E, n_shared=wl.n_shared, n_group=wl.n_group,
+                 topk_group=wl.topk_group, topk=wl.topk, afmt=afmt, wfmt=wfmt)
+    secs = time.perf_counter() - t0
+    return secs, xb.shape[0] * (wl.topk + wl.n_shared), len(experts)
+
+
+# fixed seeded token subsets of the large workloads for the oracle timing
+CPU_SAMPLE_TOKENS = 2
+
+
+def cpu_baseline(w, args):
+    """The oracle as it stands, timed on the host on bounded samples.
+
+    The headline entry is one full step of the T=8 decode workload.  The
+    per-config entries: the tiny layer in full; the prefill, skewed-prefill
+    and NVFP4 layers on a fixed seeded subset of CPU_SAMPLE_TOKENS tokens of
+    their batches (TFLOP/s extrapolated per token: the oracle's time is mostly
+    the per-expert weight decode, so the rate grows with the subset); the
+    MXFP4 -> FP8 conversion on one expert's gate/up rows (GB/s)."""
+    import synth
+    from oracle import convert as OC
+    cores = len(os.sched_getaffinity(0))
+    threads = blas_threads()
+    T = 8
+    secs, _, n_exp = _oracle_layer_timed(w, T, 1000, "bf16", "mx")
+    nbytes = n_exp * (BYTES_W13 + BYTES_W2) + 2 * T * w.H * 2 + T * w.E * 4
+    head = dict(value=nbytes / secs / 1e9, unit="GB/s", cores=cores, blas_threads=threads,
                 kind="oracle",
-                sample=(f"decode layer, one step of {T} tokens ({len(experts)} experts, {nbytes/1e6:.1f} MB of "
-                        f"weights), NumPy float64 oracle, {secs:.2f} s; weight generation excluded"))
+                sample=(f"decode layer, one step of {T} tokens ({n_exp} experts, "
+                        f"{nbytes/1e6:.1f} MB of weights), NumPy float64 oracle, {secs:.2f} s; "
+                        "weight generation excluded"))
+    per = {}
+    tw = synth.WORKLOADS["tiny"]
+    secs, pairs, _ = _oracle_layer_timed(tw, tw.T, 0, "bf16", "mx")
+    fl = pairs * (2 * tw.H * 2 * tw.I + 2 * tw.I * tw.H)
+    per["tiny"] = dict(value=fl / secs / 1e12, unit="TFLOP/s", seconds=round(secs, 3),
+                       sample=f"tiny layer in full (T={tw.T})")
+    for key, wname, seed, afmt, wfmt in (("prefill", "prefill", 2000, "mx", "mx"),
+                                         ("skewed_prefill", "skewed", 5000, "mx", "mx"),
+                                         ("nvfp4", "nvfp4", 4000, "nvfp4", "nvfp4")):
+        wl = synth.WORKLOADS[wname]
+        toks = np.sort(synth.rng(wl.wid, 90).choice(wl.T, CPU_SAMPLE_TOKENS, replace=False))
+        secs, pairs, n_exp = _oracle_layer_timed(wl, wl.T, seed, afmt, wfmt, tokens=toks)
+        per[key] = dict(value=FLOP_PER_PAIR * pairs / secs / 1e12, unit="TFLOP/s",
+                        seconds=round(secs, 2),
+                        sample=(f"tokens {toks.tolist()} of the T={wl.T} batch ({pairs} pairs, "
+                                f"{n_exp} experts), extrapolated per token"
+                                + ("; the NVFP4 tensor scales span the sample only"
+                                   if afmt == "nvfp4" else "")))
+        log(args, f"cpu baseline {key}: {per[key]['value']:.2e} TFLOP/s in {secs:.1f} s")
+    sw = synth.WORKLOADS["skewed"]
+    codes, _ = synth.expert_mx(sw, 0, 13)
+    scales, _ = synth.spanned_scales(codes.shape[0], codes.shape[1] // 16, 5, 0)
+    t0 = time.perf_counter()
+    OC.mxfp4_to_fp8_channel(codes, scales)
+    secs = time.perf_counter() - t0
+    nbytes = codes.size + scales.size + codes.size * 2 + 5 * codes.shape[0]
+    per["fp8_convert"] = dict(value=nbytes / secs / 1e9, unit="GB/s", seconds=round(secs, 2),
+                              sample=f"one expert's gate/up rows ({codes.shape[0]} x "
+                                     f"{codes.shape[1] * 2})")
+    head["per_config"] = per
+    return head
 
 
 def main():
@@ -567,6 +671,9 @@ def main():
                        kernels_ms={k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
                        workload="prefill MoE layer, T=8192, uniform routing, MXFP4 activations "
                                 "(mxfp4_quant_1x32) x MXFP4 weights, gfx950 scaled MFMA")
+    skewed = None
+    if not args.no_prefill:
+        skewed = run_skewed_mx(fm, dev_w, args.prefill_steps, torch, args)
     extra = {}
     if not args.no_extra:
         del dev_w
@@ -612,6 +719,12 @@ def main():
             "unit": "GB/s",
             "frac": round(s1["gbs"] / HBM_PEAK_GBS, 4),
             "traffic": stage1_traffic(args.tokens),
+            "traffic_source": ("stored, not measured by this run: two rocprofv3 --pmc passes "
+                               "(FETCH_SIZE, WRITE_SIZE) of this kernel on this workload, "
+                               "profiles/dq_gemm_decode_T8_hbm_counters.md; reported only while "
+                               "the kernel's sources hash as they did then"
+                               if stage1_traffic(args.tokens) is not None else
+                               "null: the kernel changed since its counters were taken"),
             "avg_launch_us": round(s1["ms"] * 1e3, 2),
             "algorithmic_bytes_per_launch": int(s1["bytes"]),
         },
@@ -621,6 +734,7 @@ def main():
         "decode_sweep": sweep,
         "ep_share": ep,
         "prefill": prefill,
+        "skewed_prefill": skewed,
         "nvfp4": extra.get("nvfp4"),
         "fp8": extra.get("fp8"),
         "dense_linear": extra.get("dense"),

@@ -1,10 +1,11 @@
 // mxfp4_to_fp8_channel: exact MXFP4 -> FP8 E4M3 per-channel conversion.
 //
-// [GAUDI] "Exact MXFP4 to FP8 per-channel conversion": per output row pick
-// one power-of-two channel scale 2^k with k = (exponent of the row's largest
-// element) - 7; each element becomes the E4M3 code of x / 2^k.  Rows whose
-// E8M0 scales span at most 9 binades convert exactly, every element an E4M3
-// normal with exponent in [-5, 7].
+// [GAUDI] "Exact MXFP4 to FP8 per-channel conversion".  For a row x of
+// decoded MXFP4 values:  e_max = floor(log2 max_i |x_i|),  k = e_max - 7,
+// channel scale = 2^k,  code_i = E4M3(x_i * 2^-k).  If the row's E8M0 codes
+// lie within 9 consecutive binades, every x_i * 2^-k is 0 or a normal E4M3
+// value with exponent in [-5, 7] (magnitude <= 1.5 * 2^7), so
+// decode(code_i) * 2^k == x_i for every element.
 //
 // The kernel is integer-only.  One wavefront converts one row in two passes
 // over its blocks (all of the row's codes held in registers):

@@ -9,7 +9,8 @@
 // staged in memory.  [GAUDI] "What was built": gate and up rows are
 // concatenated in one fused tensor (gate first, by our reading).
 //
-// Operand layout (both MFMA families): in a 16x16 MFMA tile lane l holds one
+// Operand layout of the row-major weights (the dq family and the 16x16x128
+// scaled MFMA of the mx family): in a 16x16 MFMA tile lane l holds one
 // 32-element MX block of row (l % 16), block index (l / 16) of the current
 // 128-wide K chunk.  In the natural row-major [N, K/2] layout that is exactly
 // one aligned 16-byte load per lane, with the four lanes of a row reading 64
@@ -18,20 +19,28 @@
 // column l % 16 (weight row).
 //
 // Families
-//   dq  (wfmt MXFP4 | NVFP4 | FP8; afmt BF16, or MXFP4 with FP8 weights):
-//       both operands are brought to bf16 in registers (v_cvt_scalef32_pk_*),
-//       then v_mfma_f32_16x16x32_bf16 with float32 accumulation.  The decode is
-//       exact: E2M1 x E8M0, E2M1 x E4M3 and E4M3 values all fit bf16.  A
-//       workgroup is four waves that split the K chunks round-robin and reduce
-//       through LDS, so even a single decode token spreads an expert over many
-//       CUs.  FP8 weights carry a per-row float channel scale applied in the
-//       epilogue.
-//   mx  (afmt MXFP4; wfmt MXFP4): v_mfma_scale_f32_16x16x128_f8f6f4 FP4 x FP4
-//       with the E8M0 bytes as the scale operands.
-//
-// FP8 weights with MXFP4 activations go through the bf16 path on purpose: in
-// the mixed FP4 x FP8 form of the scaled MFMA each FP4 lane holds halves of
-// two different 32-element K blocks, so one E8M0 scale per lane cannot carry
+//   dq  (wfmt MXFP4 | NVFP4 | FP8; afmt BF16, or MXFP4 with FP8 weights;
+//       block_m 16 / 32, and 64 where the dqt tiles do not apply): both operands are brought to bf16 in registers
+//       (v_cvt_scalef32_pk_*), then v_mfma_f32_16x16x32_bf16 with float32
+//       accumulation.  The decode is exact: E2M1 x E8M0, E2M1 x E4M3 and E4M3
+//       values all fit bf16.  A workgroup is four waves that split the K
+//       chunks round-robin and reduce through LDS, so even a single decode
+//       token spreads an expert over many CUs.  FP8 weights carry a per-row
+//       float channel scale applied in the epilogue.
+//   dqt (the same format pairs, and NVFP4 weights x f16 activations, with
+//       block_m 64 and fragment-major weights): the dq decode in 64-row tiles
+//       whose operands are staged through LDS (gemm_dqt.hip).
+//   mx  (afmt MXFP4; wfmt MXFP4): v_mfma_scale_f32_*_f8f6f4 FP4 x FP4 with the
+//       E8M0 bytes as the scale operands (gemm_mx.hip), up to 192 x 512 tiles.
+//   mx8 (afmt MXFP4; wfmt FP8; block_m 192): the 192-row scaled-MFMA tiles of
+//       the mx family in the FP4 x FP8 form, E4M3 weights as MFMA format 0.
+//       Only the 32x32x64 form is used: in the 16x16x128 form each FP4 lane
+//       holds halves of two different 32-element K blocks, so one E8M0 scale
+//       per lane could not carry an MX block.  The converted FP8 experts have
+//       unit block scales and one power-of-two scale per row, which the
+//       epilogue applies.  With block_m <= 64 the FP8 weights take the dq /
+//       dqt decode instead.
+
 #pragma once
 
 #include "common.h"

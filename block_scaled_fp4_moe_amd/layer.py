@@ -140,17 +140,17 @@ class MoELayer:
         T = x.shape[0]
         k = c.topk + c.n_shared
         b = self._buffers(T)
-        tick("route")
         # (one launch only when every routed expert is local: the fused call
         # permutes over the same E it routes over)
         if T <= ROUTE_PERMUTE_MAX_TOKENS and T * k <= 1024 and logits.shape[1] == c.E:
             # decode sizes: routing and permutation in one launch
+            tick("route_permute")
             _, _, perm = moe_route_permute(logits, bias, c.n_group, c.topk_group, c.topk,
                                            c.n_shared, c.block_m, c.renormalize, c.routed_scale,
                                            topk_ids=b["topk_ids"], topk_w=b["topk_w"],
                                            out=b["perm"], stream=stream)
-            tick("permute")
         else:
+            tick("route")
             moe_route(logits, bias, c.n_group, c.topk_group, c.topk, c.renormalize,
                       c.routed_scale, topk_ids=b["topk_ids"], topk_w=b["topk_w"], stream=stream)
             tick("permute")
@@ -159,7 +159,8 @@ class MoELayer:
         n_rows = perm["expert_offsets"][c.E + c.n_shared:]     # device row count
         wf = WFMT[c.wfmt]
         w = self.w
-        tick("quant1")
+        if c.afmt != "bf16":
+            tick("quant1")
         gather = dict(a_row_gather=perm["sorted_pairs"], gather_div=k)
         a_layout = A_LAYOUT_ROWMAJOR
         if c.afmt == "mx" and self.chunked:
@@ -191,7 +192,8 @@ class MoELayer:
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
                          out=b["h"] if (keep or not fused_q) else None, w_layout=self.layout,
                          a_layout=a_layout, stream=stream, **qkw, **gather, **f16kw)
-        tick("quant2")
+        if c.afmt != "bf16" and not fused_q:
+            tick("quant2")
         if fused_q:
             a2, a2s = b["hq"], b["hs"]
         elif c.afmt == "mx" and self.chunked:

@@ -214,21 +214,28 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * expert_offsets[e+1]-1; the tile list comes from moe_permute with the same
  * block_m.  A row r is read from A row a_row_gather[r] / gather_div when
  * a_row_gather != NULL (stage 1 passes sorted_pairs and k), else row r.
- * Supported (wfmt, afmt): (MXFP4, BF16), (NVFP4, BF16), (FP8, BF16),
- * (FP8, MXFP4) -- operands decoded exactly to bf16 in registers, bf16 MFMA --
- * and (MXFP4, MXFP4) -- gfx950 scaled MFMA FP4 x FP4.  K % 128 == 0,
- * N % 32 == 0 (stage 1: N % 64 == 0); block_m in {32, 64, 128, 192, 256}
- * for (MXFP4, MXFP4) with the output width a multiple of 64 (stage 1) or 128
- * (stage 2) -- block_m 128 / 256: 128 / 256, block_m 192: 256 / 512, and
- * block_m 192 only with fragment-major weights -- block_m in {16, 32, 64}
- * otherwise.  (MXFP4, MXFP4) with fragment-major weights, block_m >= 128 and
- * row-major A needs max_rows * lda / 2 < 2^32 and gathered rows < max_rows.
+ * Supported (wfmt, afmt) and block_m:
+ *   (MXFP4 | NVFP4 | FP8, BF16) and (FP8, MXFP4) with block_m in {16, 32, 64}:
+ *     both operands decoded exactly to bf16 in registers, bf16 MFMA;
+ *   (NVFP4, F16) with block_m 64 (see afmt FP4MOE_A_F16 below);
+ *   (MXFP4, MXFP4) with block_m in {32, 64, 128, 192, 256}: the gfx950
+ *     scaled MFMA, FP4 x FP4, both E8M0 scales as MFMA scale operands;
+ *   (FP8, MXFP4) with block_m 192: the gfx950 scaled MFMA in its FP4 x FP8
+ *     form (E4M3 weights, E2M1 activations, unit block scales), the per-row
+ *     channel scale applied in the epilogue.
+ * K % 128 == 0, N % 32 == 0 (stage 1: N % 64 == 0).  The output width (N/2
+ * in stage 1, N in stage 2) must be a multiple of: 64 / 128 for (MXFP4,
+ * MXFP4) at block_m 32 or 64, 128 / 256 at block_m 128 or 256, 256 / 512 at
+ * block_m 192; 128 / 256 for (FP8, MXFP4) at block_m 192 and for (NVFP4,
+ * F16).  block_m 192 needs fragment-major weights.  With fragment-major
+ * weights, block_m >= 128 and row-major A, the scaled-MFMA tiles need
+ * max_rows * lda / 2 < 2^32 and gathered rows < max_rows.
  * a_layout FP4MOE_A_LAYOUT_CHUNKED (codes and scales of a_rows rows in the
  * layout of mxfp4_quant_1x32_chunked; lda unused) is taken by (MXFP4,
- * MXFP4) with fragment-major weights and block_m 128, 192 or 256; other
- * combinations return FP4MOE_ERR_INVALID_ARG.  a_rows is in [1, 2^26] and
- * at least max_rows without a row gather; an empty batch (max_rows 0) may
- * pass a_rows 0.
+ * MXFP4) with fragment-major weights and block_m 128, 192 or 256, and by
+ * (FP8, MXFP4) with block_m 192; other combinations return
+ * FP4MOE_ERR_INVALID_ARG.  a_rows is in [1, 2^26] and at least max_rows
+ * without a row gather; an empty batch (max_rows 0) may pass a_rows 0.
  * out_q / out_q_scale (stage 1, block_m 192, MXFP4 activations, out_f32 NULL):
  * the stage-1 output h is also written quantized exactly as
  * mxfp4_quant_1x32_chunked(bf16 h, out_rows = out_q_rows) writes it -- the

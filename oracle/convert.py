@@ -2,12 +2,13 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-[GAUDI] "Exact MXFP4 to FP8 per-channel conversion": for every output row
-(channel) one power-of-two channel scale 2^k is chosen with
-k = (exponent of the row's largest element) - 7.  Each element x becomes the
-E4M3 code of x / 2^k.  When the E8M0 scales of the row span at most 9 binades
-every element is then an E4M3 normal with exponent in [-5, 7] and magnitude at
-most 192, so the conversion loses nothing.
+[GAUDI] "Exact MXFP4 to FP8 per-channel conversion".  Per output row
+(channel) x of decoded values:
+    e_max = exponent of max_i |x_i|,   k = e_max - 7,   scale = 2^k,
+    code_i = E4M3(x_i / 2^k).
+The page's claim, restated: if the row's E8M0 scales lie within 9
+consecutive binades, every x_i / 2^k is zero or an E4M3 normal with exponent
+in [-5, 7] and magnitude <= 192 = 1.5 * 2^7, so decode(code_i) * 2^k == x_i.
 
 Readings for what the page leaves open:
   * "exponent of the largest element" = floor(log2 max |x|) over the row's

@@ -428,7 +428,8 @@ def test_mxfp4_linear_full_size_sampled(gpu_lib):
     """The dense linear at the benchmarked size and launch configuration (M=16384,
     N=K=7168, activations quantized chunk-major on the device, 192 x 512 tiles):
     the activation codes and the outputs of sampled rows (first and last rows,
-    both sides of a 192-row tile boundary, random rows) against the oracle."""
+    both sides of a 192-row tile boundary, random rows) against the oracle, for
+    the float32-copy epilogue and for the bf16-only one the benchmark times."""
     M, N, K = 16384, 7168, 7168
     rng = np.random.default_rng(91)
     xb = synth.bf16_from_f32(rng.standard_normal((M, K), dtype=np.float32))
@@ -448,3 +449,10 @@ def test_mxfp4_linear_full_size_sampled(gpu_lib):
     ref = F.mxfp4_dequant(qc, qs) @ oracle_weight(wd, "mx", 0).T
     assert_float_close(host(out_f32)[rows], ref, "full-size mxfp4_linear f32 (sampled rows)")
     assert_bf16_close(bits_of(out)[rows], ref, "full-size mxfp4_linear bf16 (sampled rows)")
+    # the launch the benchmark times: bf16 output only (the epilogue that goes
+    # through LDS and leaves as 16-byte row stores)
+    del out_f32
+    out2 = torch.full((M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.mxfp4_linear(codes, scales, fc[0], fs[0], a_layout=1, M=M, out=out2)
+    assert_bf16_close(bits_of(out2)[rows], ref, "full-size mxfp4_linear, bf16-only epilogue")
+    assert not torch.isnan(out2).any().item(), "bf16-only epilogue left rows unwritten"

@@ -171,7 +171,7 @@ def test_layer_empty_batch(gpu_lib, afmt, block_m):
     assert tuple(out.shape) == (0, H)
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 8, 64])
 def test_layer_decode_full_width(gpu_lib, T):
     run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
 
@@ -189,37 +189,82 @@ def test_layer_prefill_path_full_width(gpu_lib, block_m):
 
 
 
-def test_layer_prefill_full_size_sampled(gpu_lib):
-    """The prefill layer at the benchmarked size and launch configuration
-    (T=8192, uniform routing, MXFP4 activations, 192-row tiles with h quantized
-    in the stage-1 epilogue, no intermediate copies kept): routing ids and the
-    permutation of every token bit-exact, and the outputs of sampled tokens
+def sample_tokens(perm, k, T, E, n_shared, block_m, rng, n=32):
+    """At least n tokens whose sorted rows cover: the first and last rows of the
+    most loaded routed expert's first and last M tiles, both ends of a one-tile
+    expert, both sides of the shared expert's first tile boundaries and of one
+    in its middle; random tokens fill the rest."""
+    offs = np.asarray(perm["expert_offsets"])
+    sp = np.asarray(perm["sorted_pairs"])
+    counts = np.diff(offs)
+    big = int(np.argmax(counts[:E]))
+    lo, hi = int(offs[big]), int(offs[big + 1])
+    rows = [lo, lo + block_m - 1, lo + block_m, hi - block_m - 1, hi - block_m, hi - 1]
+    one = np.flatnonzero((counts[:E] > 1) & (counts[:E] <= block_m))
+    if one.size:
+        rows += [int(offs[one[0]]), int(offs[one[0] + 1]) - 1]
+    for sh in range(E, E + n_shared):
+        o, c = int(offs[sh]), int(counts[sh])
+        for edge in (block_m, 2 * block_m, (c // 2) // block_m * block_m):
+            rows += [o + edge - 1, o + edge]
+    rows = np.array([r for r in rows if 0 <= r < offs[-1]])
+    toks = set((sp[rows] // k).tolist())
+    while len(toks) < n:
+        toks.add(int(rng.integers(T)))
+    return np.array(sorted(toks))
+
+
+def _full_size_layer(gpu_lib, wname, wfmt, seed):
+    """The MXFP4-activation layer at a benchmarked size and launch configuration
+    (192-row tiles, h quantized in the stage-1 epilogue for MXFP4 weights, no
+    intermediate copies kept): routing ids and the permutation of every token
+    bit-exact, and the outputs of at least 32 sampled tokens (sample_tokens)
     against the oracle layer run on those tokens alone (a token's output
     depends only on its own row, its routing and the weights)."""
     from oracle import permute as OP
-    w = synth.WORKLOADS["prefill"]
-    T, Et = w.T, w.E + w.n_shared
+    w = synth.WORKLOADS[wname]
+    T, Et, H, I = w.T, w.E + w.n_shared, w.H, w.I
+    k = w.topk + w.n_shared
     logits = synth.router_logits(w, T, 0)
     bias = synth.router_bias(w)
     xb = synth.activations(w, T, 0)
     rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    sub = np.array([0, T // 2 + 3, T - 1])
+    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
+    sub = sample_tokens(perm, k, T, w.E, w.n_shared, 192, np.random.default_rng(seed))
     need = set(rid[sub].reshape(-1).tolist()) | set(range(w.E, Et))
-    H, I = w.H, w.I
-    dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
-                 w13_scale=torch.empty((Et, 2 * I, H // 32), dtype=torch.uint8, device="cuda"),
-                 w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
-                 w2_scale=torch.empty((Et, H, I // 32), dtype=torch.uint8, device="cuda"))
     np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
-    for e in range(Et):                      # every expert receives tokens at this size
-        for proj, name in ((13, "w13"), (2, "w2")):
-            c, sc = synth.expert_mx(w, e, proj)
-            dev_w[name][e].copy_(torch.from_numpy(c))
-            dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
-            if e in need:
-                np_w[name][e], np_w[name + "_scale"][e] = c, sc
+    if wfmt == "mx":
+        dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
+                     w13_scale=torch.empty((Et, 2 * I, H // 32), dtype=torch.uint8, device="cuda"),
+                     w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
+                     w2_scale=torch.empty((Et, H, I // 32), dtype=torch.uint8, device="cuda"))
+        for e in range(Et):                  # every expert receives tokens at this size
+            for proj, name in ((13, "w13"), (2, "w2")):
+                c, sc = synth.expert_mx(w, e, proj)
+                dev_w[name][e].copy_(torch.from_numpy(c))
+                dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
+                if e in need:
+                    np_w[name][e], np_w[name + "_scale"][e] = c, sc
+    else:
+        # E4M3 weights: uniform bytes without the NaN patterns, power-of-two
+        # channel scales (any E4M3 operand exercises the same arithmetic as the
+        # converted experts)
+        dev_w = dict(w13=torch.empty((Et, 2 * I, H), dtype=torch.uint8, device="cuda"),
+                     w13_scale=torch.empty((Et, 2 * I), dtype=torch.float32, device="cuda"),
+                     w2=torch.empty((Et, H, I), dtype=torch.uint8, device="cuda"),
+                     w2_scale=torch.empty((Et, H), dtype=torch.float32, device="cuda"))
+        g = np.random.default_rng(97)
+        for e in range(Et):
+            for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+                c = g.integers(0, 256, (N, K), dtype=np.uint8)
+                c[(c & 0x7F) == 0x7F] = 0x3C
+                sc = np.ldexp(1.0, g.integers(-9, -3, N)).astype(np.float32)
+                dev_w[name][e].copy_(torch.from_numpy(c))
+                dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
+                if e in need:
+                    np_w[name][e], np_w[name + "_scale"][e] = c, sc
     cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt="mx",
+                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt=wfmt,
                               block_m=192)
     layer = gpu_lib.MoELayer(cfg, dev_w)
     del dev_w
@@ -227,78 +272,53 @@ def test_layer_prefill_full_size_sampled(gpu_lib):
     b = layer._bufs[T]
     assert_equal(host(b["topk_ids"]), rid, "topk_ids")
     np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
-    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
     assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
     assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
+    assert_equal(host(b["perm"]["expert_offsets"]), perm["expert_offsets"], "expert_offsets")
     ref = OL.moe_layer(xb[sub], logits[sub], bias, np_w, E=w.E, n_shared=w.n_shared,
                        n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
-                       wfmt="mx", block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
-    assert_bf16_close(bits_of(out)[sub], ref["out"], "out (sampled tokens)")
+                       wfmt=wfmt, block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
+    assert_bf16_close(bits_of(out)[sub], ref["out"], f"out ({len(sub)} sampled tokens)")
     del layer
     torch.cuda.empty_cache()
+    return np.diff(perm["expert_offsets"])
+
+
+def test_layer_prefill_full_size_sampled(gpu_lib):
+    """Prefill at T=8192 with uniform routing (see _full_size_layer)."""
+    _full_size_layer(gpu_lib, "prefill", "mx", 11)
+
+
+def test_layer_skewed_prefill_full_size_sampled(gpu_lib):
+    """The skewed prefill at T=16384: Zipf(1.1) expert popularity, MXFP4 x MXFP4
+    on 192-row tiles (see _full_size_layer).  The most loaded expert spans many
+    M tiles; its first and last tiles are among the sampled rows."""
+    counts = _full_size_layer(gpu_lib, "skewed", "mx", 12)
+    assert counts[:384].max() > 8 * 192          # the routing really is skewed
 
 
 def test_layer_fp8_full_size_sampled(gpu_lib):
-    """The FP8-weight layer at the benchmarked size and launch configuration
-    (T=16384, Zipf(1.1) routing, MXFP4 activations x E4M3 weights with
-    power-of-two channel scales on the 192-row scaled-MFMA tiles): routing and
-    permutation of every token bit-exact, sampled token outputs against the
-    oracle layer run on those tokens alone.  The E4M3 codes are uniform bytes
-    without the NaN patterns (any E4M3 operand exercises the same arithmetic as
-    the converted experts)."""
-    from oracle import permute as OP
-    w = synth.WORKLOADS["skewed"]
-    T, Et, H, I = w.T, w.E + w.n_shared, w.H, w.I
-    logits = synth.router_logits(w, T, 0)
-    bias = synth.router_bias(w)
-    xb = synth.activations(w, T, 0)
-    rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    sub = np.array([0, T // 3, T - 1])
-    need = set(rid[sub].reshape(-1).tolist()) | set(range(w.E, Et))
-    dev_w = dict(w13=torch.empty((Et, 2 * I, H), dtype=torch.uint8, device="cuda"),
-                 w13_scale=torch.empty((Et, 2 * I), dtype=torch.float32, device="cuda"),
-                 w2=torch.empty((Et, H, I), dtype=torch.uint8, device="cuda"),
-                 w2_scale=torch.empty((Et, H), dtype=torch.float32, device="cuda"))
-    np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
-    g = np.random.default_rng(97)
-    for e in range(Et):
-        for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
-            c = g.integers(0, 256, (N, K), dtype=np.uint8)
-            c[(c & 0x7F) == 0x7F] = 0x3C
-            sc = np.ldexp(1.0, g.integers(-9, -3, N)).astype(np.float32)
-            dev_w[name][e].copy_(torch.from_numpy(c))
-            dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
-            if e in need:
-                np_w[name][e], np_w[name + "_scale"][e] = c, sc
-    cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt="fp8",
-                              block_m=192)
-    layer = gpu_lib.MoELayer(cfg, dev_w)
-    del dev_w
-    out = layer.forward(bf16_dev(xb), dev(logits), dev(bias))
-    b = layer._bufs[T]
-    assert_equal(host(b["topk_ids"]), rid, "topk_ids")
-    np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
-    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
-    assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
-    assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
-    ref = OL.moe_layer(xb[sub], logits[sub], bias, np_w, E=w.E, n_shared=w.n_shared,
-                       n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
-                       wfmt="fp8", block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
-    assert_bf16_close(bits_of(out)[sub], ref["out"], "out (sampled tokens)")
-    del layer
-    torch.cuda.empty_cache()
+    """The FP8-weight layer at T=16384 with Zipf(1.1) routing: MXFP4 activations
+    x E4M3 weights with power-of-two channel scales on the 192-row FP4 x FP8
+    scaled-MFMA tiles (see _full_size_layer)."""
+    _full_size_layer(gpu_lib, "skewed", "fp8", 13)
 
 
 def test_layer_nvfp4_full_size_sampled(gpu_lib):
     """The NVFP4 emulation layer at the benchmarked size and launch configuration
-    (T=2048, 64-row tiles, activations in the f16 operand form): routing and
-    permutation of every token bit-exact, the activation QDQ of every token
-    bit-exact, and sampled rows of h against the oracle's stage 1.  The second
-    QDQ takes one tensor scale over all of h, which couples every token, so the
-    final outputs are checked at full width on fewer tokens instead
-    (test_layer_nvfp4_full_width).  Weights: uniform code bytes, positive
-    finite E4M3 block scales, tensor scales U(0.01, 0.02)."""
+    (T=2048, 64-row tiles, activations in the f16 operand form), stage by stage
+    on the GPU's own upstream outputs (the second QDQ's tensor scale spans all
+    of h and couples every token, so each stage is checked on what the GPU fed
+    it):
+      * routing and permutation of every token bit-exact;
+      * the activation QDQ of every token bit-exact;
+      * stage 1 on sampled sorted rows against the oracle's stage 1;
+      * the second QDQ of every row of the GPU's h bit-exact;
+      * stage 2 on sampled sorted rows against the oracle run on the GPU's
+        QDQ'd h;
+      * the combine of sampled tokens against the oracle run on the GPU's y.
+    Weights: uniform code bytes, positive finite E4M3 block scales, tensor
+    scales U(0.01, 0.02)."""
     from oracle import formats as F
     from oracle import gemm as OG
     from oracle import permute as OP
@@ -313,23 +333,30 @@ def test_layer_nvfp4_full_size_sampled(gpu_lib):
     perm = OP.moe_permute(rid, w.E, w.n_shared, 64)
     offs = perm["expert_offsets"]
     counts = np.diff(offs)
-    # sampled sorted rows: first and last row of the most loaded expert, of a
-    # one-row expert if any, and random rows
+    n_rows = int(offs[-1])
+    # sampled sorted rows: the first and last rows of the most loaded expert
+    # and of its first and last 64-row tiles, both ends of a one-tile expert,
+    # a one-row expert if any, and random rows
     g = np.random.default_rng(98)
     big = int(np.argmax(counts))
-    rows = [offs[big], offs[big + 1] - 1]
+    lo, hi = int(offs[big]), int(offs[big + 1])
+    rows = [lo, lo + 63, lo + 64, hi - 65, hi - 64, hi - 1]
+    one = np.flatnonzero((counts > 1) & (counts <= 64))
+    if one.size:
+        rows += [int(offs[one[0]]), int(offs[one[0] + 1]) - 1]
     single = np.flatnonzero(counts == 1)
     if single.size:
-        rows.append(offs[single[0]])
-    rows = np.unique(np.concatenate([rows, g.choice(int(offs[-1]), 9, replace=False)]))
+        rows.append(int(offs[single[0]]))
+    rows = np.unique(np.concatenate([rows, g.choice(n_rows, 16, replace=False)]))
     row_e = np.searchsorted(offs, rows, side="right") - 1
+    toks = np.unique(perm["sorted_pairs"][rows] // k)
     dev_w = dict(w13=torch.empty((Et, 2 * I, H // 2), dtype=torch.uint8, device="cuda"),
                  w13_scale=torch.empty((Et, 2 * I, H // 16), dtype=torch.uint8, device="cuda"),
                  w2=torch.empty((Et, H, I // 2), dtype=torch.uint8, device="cuda"),
                  w2_scale=torch.empty((Et, H, I // 16), dtype=torch.uint8, device="cuda"))
     ts = {"w13": g.uniform(0.01, 0.02, Et).astype(np.float32),
           "w2": g.uniform(0.01, 0.02, Et).astype(np.float32)}
-    w13 = {}
+    kept = {"w13": {}, "w2": {}}
     sampled_experts = set(row_e.tolist())
     for e in range(Et):
         for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
@@ -337,8 +364,8 @@ def test_layer_nvfp4_full_size_sampled(gpu_lib):
             sc = g.integers(0x01, 0x7F, (N, K // 16), dtype=np.uint8)   # positive finite E4M3
             dev_w[name][e].copy_(torch.from_numpy(c))
             dev_w[name + "_scale"][e].copy_(torch.from_numpy(sc))
-            if name == "w13" and e in sampled_experts:
-                w13[e] = (c, sc)
+            if e in sampled_experts:
+                kept[name][e] = (c, sc)
     dev_w["w13_ts"], dev_w["w2_ts"] = dev(ts["w13"]), dev(ts["w2"])
     cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                               topk_group=w.topk_group, topk=w.topk, afmt="nvfp4", wfmt="nvfp4",
@@ -355,16 +382,38 @@ def test_layer_nvfp4_full_size_sampled(gpu_lib):
     y_ref = F.bf16_decode(qx["y"])
     y_gpu = host(b["xq"]).astype(np.float64) * float(host(b["xs"])[0])
     assert np.array_equal(y_gpu, y_ref), "activation QDQ (f16 form)"
+    del qx, y_gpu
     # stage 1 on sampled sorted rows
     tok = perm["sorted_pairs"][rows] // k
-    h_gpu = bits_of(b["h"])[rows]
+    h_all = bits_of(b["h"])[:n_rows]
     ref = np.empty((len(rows), I))
-    for i, (r, e) in enumerate(zip(rows, row_e)):
-        c, sc = w13[int(e)]
+    for i, e in enumerate(row_e):
+        c, sc = kept["w13"][int(e)]
         wd = OG.dequant_expert("nvfp4", c, sc, ts["w13"][e])
         ref[i] = OG.stage1_expert(y_ref[tok[i]][None, :], wd)[0]
-    assert_bf16_close(h_gpu, ref, "h (sampled rows)")
-    del layer, b
+    assert_bf16_close(h_all[rows], ref, "h (sampled rows)")
+    del y_ref
+    # the second QDQ over every row of the GPU's own h, bit-exact
+    qh = OQ.nvfp4_qdq(h_all)
+    a2_ref = F.bf16_decode(qh["y"])
+    a2_gpu = host(b["hq"])[:n_rows].astype(np.float64) * float(host(b["hs"])[0])
+    assert np.array_equal(a2_gpu, a2_ref), "second QDQ (f16 form) over every row of h"
+    del qh, a2_gpu, h_all
+    # stage 2 on sampled sorted rows, fed the QDQ'd GPU h
+    y_all = bits_of(b["y"])
+    ref = np.empty((len(rows), H))
+    for i, e in enumerate(row_e):
+        c, sc = kept["w2"][int(e)]
+        wd = OG.dequant_expert("nvfp4", c, sc, ts["w2"][e])
+        ref[i] = OG.stage2_expert(a2_ref[rows[i]][None, :], wd)[0]
+    assert_bf16_close(y_all[rows], ref, "y (sampled rows)")
+    del a2_ref
+    # the combine of sampled tokens, fed the GPU's y
+    pos = np.asarray(perm["pair_pos"]).reshape(T, k)[toks].reshape(-1)
+    out_ref, _ = OG.moe_combine(F.bf16_decode(y_all), pos, rw[toks], len(toks), w.topk,
+                                w.n_shared)
+    assert_bf16_close(bits_of(b["out"])[toks], out_ref, f"out ({len(toks)} sampled tokens)")
+    del layer, b, y_all
     torch.cuda.empty_cache()
 
 

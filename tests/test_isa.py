@@ -148,3 +148,33 @@ def test_no_scalar_cache_writes():
                      r"dcache_discard)")
     hits = [(n, ln) for n, (lines, _) in kernels().items() for ln in lines if bad.match(ln)]
     assert not hits, hits[:5]
+
+
+def _reg_range(tok):
+    """'v[4:7]' -> ('v', 4, 7); 'v12' -> ('v', 12, 12); otherwise None."""
+    m = re.match(r"^([va])\[(\d+):(\d+)\]$", tok) or re.match(r"^([va])(\d+)()$", tok)
+    if not m:
+        return None
+    lo = int(m.group(2))
+    return m.group(1), lo, int(m.group(3)) if m.group(3) else lo
+
+
+def test_mfma_destination_disjoint_from_sources():
+    """Every MFMA of every kernel writes a register range that overlaps neither
+    its A nor its B operand: FP8-operand MFMAs generated with an overlapping
+    destination gave wrong results, so the kernels keep them apart and this
+    guards against a compiler or flag change that would not."""
+    bad, n = [], 0
+    for name, (lines, _) in kernels().items():
+        for ln in lines:
+            if not ln.startswith("v_mfma"):
+                continue
+            ops = [t.strip() for t in ln.split("//")[0].split(None, 1)[1].split(",")]
+            dst, a, b = (_reg_range(ops[0].split()[0]), _reg_range(ops[1]), _reg_range(ops[2]))
+            assert dst and a and b, f"{name}: cannot parse {ln}"
+            n += 1
+            for src in (a, b):
+                if src[0] == dst[0] and src[1] <= dst[2] and dst[1] <= src[2]:
+                    bad.append((name, ln))
+    assert n > 0
+    assert not bad, bad[:3]
