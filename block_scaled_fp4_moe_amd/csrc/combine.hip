@@ -22,11 +22,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
                                                       const float* __restrict__ topk_w, int topk,
                                                       int n_shared, int H,
                                                       uint16_t* __restrict__ out,
-                                                      float* __restrict__ out_f32) {
-  const int64_t t = blockIdx.y;
+                                                      float* __restrict__ out_f32, int T) {
   const int col = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (col >= H) return;
   const int k = topk + n_shared;
+  // grid y covers at most 65535 tokens; each y index strides over the rest
+  for (int64_t t = blockIdx.y; t < T; t += gridDim.y) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -64,6 +65,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     of[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     of[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
+  }
 }
 
 }  // namespace fp4moe
@@ -75,7 +77,6 @@ extern "C" int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, co
                            void* stream) {
   FP4MOE_REQUIRE(T >= 0 && topk >= 1 && n_shared >= 0 && H > 0 && H % 8 == 0,
                  "moe_combine: T=%d topk=%d n_shared=%d H=%d (H %% 8 != 0)", T, topk, n_shared, H);
-  FP4MOE_REQUIRE(T <= 65535, "moe_combine: T=%d above 65535", T);
   if (T == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(y_sorted && pair_pos && topk_w && out, "moe_combine: null pointer");
   FP4MOE_REQUIRE(((uintptr_t)y_sorted & 15) == 0 && ((uintptr_t)out & 15) == 0 &&
@@ -83,8 +84,8 @@ extern "C" int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, co
                  "moe_combine: y, out and out_f32 must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
   const int lanes = H / 8;
-  dim3 grid((lanes + 255) / 256, T);
+  dim3 grid((lanes + 255) / 256, T < 65535 ? T : 65535);
   hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, as_stream(stream), y_sorted, pair_pos,
-                     topk_w, topk, n_shared, H, out, out_f32);
+                     topk_w, topk, n_shared, H, out, out_f32, T);
   return check_launch("moe_combine");
 }

@@ -186,11 +186,14 @@ def test_linear_rejects_bad_arguments():
     assert run(M=0, layout=1, stride=0)[0] == 0
 
 
-def test_combine_rejects_too_many_tokens():
+def test_combine_takes_more_than_65535_tokens():
+    """The token count has no cap below the int range: T = 65536 passes the
+    argument checks (on a host without a gfx950 device the call then stops at
+    the device check, before any launch)."""
     fake = ctypes.c_void_p(4096)
     st, msg = _status(lambda lib: lib.moe_combine(fake, fake, fake, 65536, 8, 1, 64, fake, None,
                                                    None))
-    assert st == 1 and "65535" in msg
+    assert st != 1, msg
 
 
 def test_too_small_workspace_is_reported():
@@ -218,3 +221,4 @@ def test_preshuffle_rejects_bad_shapes():
     assert st == 1
     assert _status(lambda lib: lib.fp4_weight_preshuffle(0, 0, 32, 256, None, None, None, None,
                                                           None))[0] == 0
+

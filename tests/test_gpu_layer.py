@@ -17,7 +17,7 @@ from oracle import convert as OC
 from oracle import layer as OL
 from oracle import route as OR
 
-from .parity import assert_bf16_close, assert_equal
+from .parity import assert_bf16_close, assert_equal, assert_float_close
 from .test_gpu_kernels import bf16_dev, bits_of, dev, host
 
 pytestmark = pytest.mark.gpu
@@ -214,14 +214,36 @@ def sample_tokens(perm, k, T, E, n_shared, block_m, rng, n=32):
     return np.array(sorted(toks))
 
 
+# End-to-end drift bound of the MXFP4-activation layers.  h is re-quantized to
+# MXFP4 between the stages, so a rounding-boundary flip of one h value (float32
+# accumulation on the GPU against float64 in the oracle) moves a whole FP4
+# code and compounds through stage 2; each stage is therefore held to the
+# float tolerance on the GPU's own upstream outputs, and the end-to-end
+# difference only to this looser bound.
+END_TO_END_REL_L2 = 5e-3
+
+
 def _full_size_layer(gpu_lib, wname, wfmt, seed):
     """The MXFP4-activation layer at a benchmarked size and launch configuration
-    (192-row tiles, h quantized in the stage-1 epilogue for MXFP4 weights, no
-    intermediate copies kept): routing ids and the permutation of every token
-    bit-exact, and the outputs of at least 32 sampled tokens (sample_tokens)
-    against the oracle layer run on those tokens alone (a token's output
-    depends only on its own row, its routing and the weights)."""
+    (192-row tiles, h quantized in the stage-1 epilogue; the bf16 copy of h is
+    also kept for the check).  Every token: routing ids and the permutation
+    bit-exact.  At least 32 sampled tokens (sample_tokens), stage by stage on
+    the GPU's own upstream outputs (a token's rows depend only on its own row,
+    its routing and the weights):
+      * the activation codes and scales bit-exact;
+      * stage 1 (h, on whole 32-blocks of columns) against the oracle's stage 1;
+      * the epilogue's MXFP4 codes of h (full rows) bit-exact against the
+        oracle's quantizer applied to the GPU's h;
+      * stage 2 (y, on 512 columns) against the oracle fed the GPU's full h
+        codes;
+      * the combine (full rows) against the oracle fed the GPU's y;
+    and, on four of the tokens, the end-to-end output against the oracle layer
+    within END_TO_END_REL_L2.  Only the checked weight rows are decoded, each
+    expert once, so the oracle side stays within about a minute."""
+    from oracle import formats as F
+    from oracle import gemm as OG
     from oracle import permute as OP
+    from oracle import quant as OQ
     w = synth.WORKLOADS[wname]
     T, Et, H, I = w.T, w.E + w.n_shared, w.H, w.I
     k = w.topk + w.n_shared
@@ -268,18 +290,86 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
                               block_m=192)
     layer = gpu_lib.MoELayer(cfg, dev_w)
     del dev_w
-    out = layer.forward(bf16_dev(xb), dev(logits), dev(bias))
-    b = layer._bufs[T]
+    b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
     assert_equal(host(b["topk_ids"]), rid, "topk_ids")
     np.testing.assert_allclose(host(b["topk_w"]), rw, rtol=1e-6)
     assert_equal(host(b["perm"]["sorted_pairs"]), perm["sorted_pairs"], "sorted_pairs")
     assert_equal(host(b["perm"]["pair_pos"]), perm["pair_pos"], "pair_pos")
     assert_equal(host(b["perm"]["expert_offsets"]), perm["expert_offsets"], "expert_offsets")
-    ref = OL.moe_layer(xb[sub], logits[sub], bias, np_w, E=w.E, n_shared=w.n_shared,
+    # the sampled tokens' sorted rows, slot by slot
+    pos = np.asarray(perm["pair_pos"]).reshape(T, k)[sub]            # [n_sub, k]
+    rows = pos.reshape(-1)
+    row_e = np.searchsorted(perm["expert_offsets"], rows, side="right") - 1
+    rows_d = torch.from_numpy(rows.astype(np.int64)).cuda()
+
+    def chunked_rows(codes, scales):          # [K/128, P, 64|4] -> row-major [n, K/2], [n, K/32]
+        c = codes.index_select(1, rows_d).permute(1, 0, 2).reshape(len(rows), -1)
+        s_ = scales.index_select(1, rows_d).permute(1, 0, 2).reshape(len(rows), -1)
+        return host(c), host(s_)
+
+    def weight(name, e, wrows):
+        """Rows wrows of expert e's dequantized weight (float64)."""
+        return OG.dequant_expert(wfmt, np_w[name][e][wrows], np_w[name + "_scale"][e][wrows])
+
+    def per_expert(name, wrows, inputs, fn):
+        """fn(inputs of the rows of one expert, its weight rows) for every
+        expert of the sampled rows, each expert's weights decoded once."""
+        out = None
+        for e in np.unique(row_e):
+            idx = np.flatnonzero(row_e == e)
+            r = fn(inputs[idx], weight(name, int(e), wrows))
+            if out is None:
+                out = np.empty((len(rows), r.shape[1]))
+            out[idx] = r
+        return out
+
+    # checked columns: whole 32-blocks of h (first, last and random ones) and
+    # 512 columns of y (first and last 64 and random ones); stage 2 still
+    # consumes the GPU's full h rows
+    g = np.random.default_rng(seed + 100)
+    hb = np.unique(np.concatenate([[0, I // 32 - 1], g.choice(I // 32, 6, replace=False)]))
+    h_cols = (hb[:, None] * 32 + np.arange(32)).reshape(-1)
+    y_cols = np.unique(np.concatenate([np.arange(64), np.arange(H - 64, H),
+                                       g.choice(H, 384, replace=False)]))
+    # activation codes of the sampled tokens (written to each of their rows)
+    xc, xs = chunked_rows(b["xq"], b["xs"])
+    qc, qs = OQ.mxfp4_quant_1x32(xb[sub])
+    assert_equal(xc, np.repeat(qc, k, axis=0), "activation codes (sampled rows)")
+    assert_equal(xs, np.repeat(qs, k, axis=0), "activation scales (sampled rows)")
+    a1 = np.repeat(F.mxfp4_dequant(qc, qs), k, axis=0)
+    print(f"[{wname}/{wfmt}] {len(sub)} tokens, {len(rows)} rows, "
+          f"{len(np.unique(row_e))} experts: activation codes ok", flush=True)
+    # stage 1 on the checked h columns (gate rows h_cols, up rows I + h_cols)
+    h_gpu = host(b["h"].index_select(0, rows_d).view(torch.int16)).view(np.uint16)
+    wr13 = np.concatenate([h_cols, I + h_cols])
+    h_ref = per_expert("w13", wr13, a1, lambda a, wt: OG.stage1_expert(a, wt))
+    assert_bf16_close(h_gpu[:, h_cols], h_ref, "h (sampled rows, checked columns)")
+    print(f"[{wname}/{wfmt}] stage 1 ok", flush=True)
+    # the epilogue's MXFP4 codes of h, full rows
+    hc, hs = chunked_rows(b["hq"], b["hs"])
+    rc, rs = OQ.mxfp4_quant_1x32(h_gpu)
+    assert_equal(hc, rc, "h codes from the stage-1 epilogue (sampled rows)")
+    assert_equal(hs, rs, "h scales from the stage-1 epilogue (sampled rows)")
+    a2 = F.mxfp4_dequant(hc, hs)
+    # stage 2 on the GPU's h codes, checked y columns
+    y_gpu = host(b["y"].index_select(0, rows_d).view(torch.int16)).view(np.uint16)
+    y_ref = per_expert("w2", y_cols, a2, lambda a, wt: OG.stage2_expert(a, wt))
+    assert_bf16_close(y_gpu[:, y_cols], y_ref, "y (sampled rows, checked columns)")
+    print(f"[{wname}/{wfmt}] h codes and stage 2 ok", flush=True)
+    # the combine on the GPU's y, full rows (rows of token i are i*k .. i*k+k-1)
+    out_ref, _ = OG.moe_combine(F.bf16_decode(y_gpu), np.arange(len(rows)), rw[sub], len(sub),
+                                w.topk, w.n_shared)
+    out_gpu = bits_of(b["out"])[sub]
+    assert_bf16_close(out_gpu, out_ref, f"out ({len(sub)} sampled tokens, GPU y)")
+    # end to end on four of the tokens
+    e2e = sub[:: max(1, len(sub) // 4)][:4]
+    ref = OL.moe_layer(xb[e2e], logits[e2e], bias, np_w, E=w.E, n_shared=w.n_shared,
                        n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
-                       wfmt=wfmt, block_m=192, topk_ids=rid[sub], topk_w=rw[sub])
-    assert_bf16_close(bits_of(out)[sub], ref["out"], f"out ({len(sub)} sampled tokens)")
-    del layer
+                       wfmt=wfmt, block_m=192, topk_ids=rid[e2e], topk_w=rw[e2e])
+    stats = assert_float_close(F.bf16_decode(bits_of(b["out"])[e2e]), F.bf16_round(ref["out"]),
+                               "out end to end", rel_l2=END_TO_END_REL_L2, max_abs_rms=1.0)
+    print(f"[{wname}/{wfmt}] combine ok; end-to-end rel-L2 {stats['rel_l2']:.2e}", flush=True)
+    del layer, b
     torch.cuda.empty_cache()
     return np.diff(perm["expert_offsets"])
 
