@@ -67,6 +67,8 @@ def load():
         "moe_permute_max_tiles": ([I, I, I, I, I], I),
         "moe_permute_workspace": ([I, I, I, I, I], S),
         "moe_permute": ([P, I, I, I, I, I, P, S, P, P, P, P, P, P, P], I),
+        "moe_permute_noalloc_max_workspace": ([], S),
+        "moe_permute_noalloc": ([P, I, I, I, I, I, P, P, P, P, P, P, P], I),
         "moe_route_permute": ([P, P, I, I, I, I, I, I, F, I, I, P, P, P, P, P, P, P, P, P], I),
         "mxfp4_quant_1x32": ([P, I, I, I64, P, P, P, P, P], I),
         "mxfp4_quant_1x32_chunked": ([P, I, I, I64, P, I, I, P, P, P, P], I),
@@ -158,6 +160,20 @@ def moe_permute(topk_ids, E, n_shared, block_m, workspace=None, out=None, stream
                            _p(out["expert_offsets"]), _p(out["sorted_pairs"]), _p(out["pair_pos"]),
                            _p(out["tiles"]), _p(out["n_tiles"]), _p(out["n_dropped"]),
                            _stream(stream)))
+    return out
+
+
+def moe_permute_noalloc(topk_ids, E, n_shared, block_m, out, stream=None):
+    """moe_permute without a workspace argument: the library's own per-device
+    buffer holds the chunk histograms.  `out` holds the caller's output
+    tensors (the dict moe_permute returns); nothing is allocated here."""
+    lib = load()
+    T, topk = topk_ids.shape
+    assert topk_ids.is_contiguous()
+    _check(lib.moe_permute_noalloc(_p(topk_ids), T, topk, E, n_shared, block_m,
+                                   _p(out["expert_offsets"]), _p(out["sorted_pairs"]),
+                                   _p(out["pair_pos"]), _p(out["tiles"]), _p(out["n_tiles"]),
+                                   _p(out["n_dropped"]), _stream(stream)))
     return out
 
 

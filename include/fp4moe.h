@@ -129,6 +129,27 @@ int moe_permute(const int32_t* topk_ids, int T, int topk, int E, int n_shared, i
                 int32_t* n_dropped, void* stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs and errors as moe_permute
+ * without the workspace: the per-chunk histograms of large batches live in a
+ * buffer the library owns, one per device, of
+ * moe_permute_noalloc_max_workspace() bytes (4 MiB), held until the process
+ * ends.  A batch whose moe_permute_workspace() exceeds that returns
+ * FP4MOE_ERR_WORKSPACE before any launch (with E + n_shared = 385 the limit
+ * is about 2.8 M pairs).  The call allocates nothing; the first call on a
+ * device looks up the buffer's device address.  Every call on one device
+ * shares that device's buffer, so calls that overlap on one device (on
+ * different streams without ordering between them) race; calls ordered on
+ * one stream do not.
+ */
+size_t moe_permute_noalloc_max_workspace(void);
+int moe_permute_noalloc(const int32_t* topk_ids, int T, int topk, int E, int n_shared,
+                        int block_m, int32_t* expert_offsets, int32_t* sorted_pairs,
+                        int32_t* pair_pos, int32_t* tiles, int32_t* n_tiles, int32_t* n_dropped,
+                        void* stream);
+
+/*
  * moe_route_permute -- moe_route followed by moe_permute in one launch, for
  * decode-sized batches: T*(topk+n_shared) <= 1024.  [GAUDI] "What was built"
  * (the router) and [NVFP4] "Memory Management" (the dispatch), as for the two

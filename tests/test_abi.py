@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 18, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
               "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked",
               "moe_route_permute", "mxfp4_linear"]:
@@ -222,3 +222,16 @@ def test_preshuffle_rejects_bad_shapes():
     assert _status(lambda lib: lib.fp4_weight_preshuffle(0, 0, 32, 256, None, None, None, None,
                                                           None))[0] == 0
 
+
+def test_permute_noalloc_rejects_batches_beyond_its_buffer():
+    """The library-owned histogram buffer is 4 MiB: a batch needing more is
+    refused before any device work (the pointers are never dereferenced)."""
+    lib = fm.load()
+    cap = lib.moe_permute_noalloc_max_workspace()
+    assert cap == 4 << 20
+    T, topk, E, ns, bm = 40000, 8, 4000, 0, 64
+    assert lib.moe_permute_workspace(T, topk, E, ns, bm) > cap
+    p = ctypes.c_void_p(256)
+    st, msg = _status(lambda lib: lib.moe_permute_noalloc(p, T, topk, E, ns, bm, p, p, p, p, p, p,
+                                                          None))
+    assert st == 3 and "moe_permute_noalloc" in msg and "4194304" in msg
