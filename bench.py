@@ -48,27 +48,20 @@ FP8_BLOCK_M = 192              # FP8-weight layer: 192-row tiles on the scaled M
 METRIC = "FP4 MoE layer TFLOP/s (prefill) + weight GB/s (decode) on 1 MI355X"
 N_ROTATE = 16
 
-# HBM traffic of the stage-1 decode kernel on the T=8 workload, from two
+# HBM traffic of the roofline kernel on the T=8 decode workload, from two
 # rocprofv3 counter passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch,
 # mean over the rotated routing draws), each scaled by what that counter reads
 # for a plain 1 GiB copy (FETCH_SIZE reads half the bytes: x1.9999; WRITE_SIZE
-# x1.0).  Reported only while the kernel sources hash to what they were when
-# the counters were taken; otherwise traffic is null.
-STAGE1_COUNTERS = dict(
-    tokens=8, fetch_kib=378987.9, write_kib=288.0, fetch_scale=1.9999, write_scale=1.0,
-    sources=("block_scaled_fp4_moe_amd/csrc/gemm_dq.hip",
-             "block_scaled_fp4_moe_amd/csrc/gemm_common.h",
-             "block_scaled_fp4_moe_amd/csrc/common.h"),
-    sha256=("0076bca361457f70e306af6c4a4b1799751db10cd903e4e2d28bd2b6ee78d612",
-            "cf8f48c52be477ced44cebd1615393bfffd83690f565a39b7d56f6997436c8f1",
-            "3af844087c30bbbc3272119b6ca934e877d90b1159a2b45ad9077007c79fd1c0"))
+# x1.0).  Reported only while the kernel's sources hash to what they were when
+# the counters were taken; otherwise traffic is null.  Keyed by kernel.
+ROOFLINE_COUNTERS = {}
 
 
-def stage1_traffic(tokens):
-    """Counter-derived HBM bytes per stage-1 launch, or None if stale."""
+def roofline_traffic(kernel, tokens):
+    """Counter-derived HBM bytes per launch of `kernel`, or None if stale or absent."""
     import hashlib
-    c = STAGE1_COUNTERS
-    if tokens != c["tokens"]:
+    c = ROOFLINE_COUNTERS.get(kernel)
+    if c is None or tokens != c["tokens"]:
         return None
     root = os.path.dirname(os.path.abspath(__file__))
     for rel, want in zip(c["sources"], c["sha256"]):
@@ -223,10 +216,13 @@ def decode_bytes(cfg, T, touched):
     return touched * (BYTES_W13 + BYTES_W2) + 2 * T * cfg.H * 2 + T * cfg.E * 4
 
 
-def run_decode(fm, w, dev_w, T, steps, warmup, torch, args):
+def run_decode(fm, w, dev_w, T, steps, warmup, torch, args, fused=False):
+    """The decode layer at T tokens: the chain of calls, or with `fused` the
+    single launch (moe_decode_fused)."""
     import synth
     cfg = fm.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                         topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx", block_m=16)
+                         topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx", block_m=16,
+                         fused_decode=fused)
     layer = fm.MoELayer(cfg, dev_w, preshuffled=True)
     bias = torch.from_numpy(synth.router_bias(w)).cuda()
     batches = [batch_inputs(w, T, 1000 + i, torch) for i in range(N_ROTATE)]
@@ -234,12 +230,19 @@ def run_decode(fm, w, dev_w, T, steps, warmup, torch, args):
     step_bytes = decode_bytes(cfg, T, r["touched_per_step"])
     r["gbs"] = step_bytes / (r["ms_per_step"] * 1e-3) / 1e9
     r["bytes_per_step"] = step_bytes
-    # dominant kernel: stage-1 gate/up GEMM; algorithmic bytes per launch =
-    # touched experts x W13 bytes + gathered activations in + h out
+    # dominant kernel: the single-launch layer (its algorithmic bytes per
+    # launch are the step's: touched experts' weights + x in + out + logits),
+    # else the stage-1 gate/up GEMM of the chain (touched experts x W13 bytes
+    # + gathered activations in + h out)
     k = w.topk + w.n_shared
-    s1_bytes = r["touched_per_step"] * BYTES_W13 + T * cfg.H * 2 + T * k * cfg.I * 2
-    s1_ms = r["per_kernel_ms"]["stage1"]
-    r["stage1"] = dict(ms=s1_ms, bytes=s1_bytes, gbs=s1_bytes / (s1_ms * 1e-3) / 1e9)
+    if "fused" in r["per_kernel_ms"]:
+        rk, rk_bytes, rk_ms = "fused", step_bytes, r["per_kernel_ms"]["fused"]
+    else:
+        rk = "stage1"
+        rk_bytes = r["touched_per_step"] * BYTES_W13 + T * cfg.H * 2 + T * k * cfg.I * 2
+        rk_ms = r["per_kernel_ms"]["stage1"]
+    r["roofline_kernel"] = dict(name=rk, ms=rk_ms, bytes=rk_bytes,
+                                gbs=rk_bytes / (rk_ms * 1e-3) / 1e9)
     # step-time spread (one event pair per step) and the cold-cache figure
     r["spread"] = {}
     for mode, d in r["dist"].items():
@@ -660,6 +663,18 @@ def main():
                                       experts_per_step=round(r["touched_per_step"], 1),
                                       frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
                                       step_spread=r["spread"])
+    single = {}
+    if not args.no_sweep:
+        # the same decode batches through the single-launch layer
+        # (moe_decode_fused), for comparison with the chain of calls
+        for T in (args.tokens, 1):
+            if T > 16:
+                continue
+            r = run_decode(fm, w, dev_w, T, args.steps, args.warmup, torch, args, fused=True)
+            single[f"T{T}"] = dict(gbs=round(r["gbs"], 1), us_per_step=round(r["ms_per_step"] * 1e3, 2),
+                                  frac=round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                  kernels_us={k2: round(v * 1e3, 2)
+                                              for k2, v in r["per_kernel_ms"].items()})
     ep = None
     if not args.no_sweep:
         ep = run_ep_share(fm, w, dev_w, args.tokens, args.steps, args.warmup, torch, args)
@@ -687,7 +702,10 @@ def main():
         cpu = cpu_baseline(w, args)
         log(args, f"cpu baseline: {cpu['value']:.3f} GB/s ({cpu['sample']})")
 
-    s1 = head["stage1"]
+    s1 = head["roofline_kernel"]
+    rk_desc = {"fused": "moe_decode_fused (the whole layer in one launch)",
+               "stage1": "fp4_grouped_gemm stage 1 (gate/up + SiLU*up), dq path"}[s1["name"]]
+    traffic = roofline_traffic(s1["name"], args.tokens)
     line = {
         "metric": METRIC,
         "value": round(head["gbs"], 1),
@@ -712,19 +730,18 @@ def main():
             "weight_layout": "fragment-major (fp4_weight_preshuffle, once at load)",
         },
         "roofline": {
-            "kernel": "fp4_grouped_gemm stage 1 (gate/up + SiLU*up), dq path",
+            "kernel": rk_desc,
             "bound": "hbm",
             "achieved": round(s1["gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(s1["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": stage1_traffic(args.tokens),
+            "traffic": traffic,
             "traffic_source": ("stored, not measured by this run: two rocprofv3 --pmc passes "
                                "(FETCH_SIZE, WRITE_SIZE) of this kernel on this workload, "
-                               "profiles/dq_gemm_decode_T8_hbm_counters.md; reported only while "
-                               "the kernel's sources hash as they did then"
-                               if stage1_traffic(args.tokens) is not None else
-                               "null: the kernel changed since its counters were taken"),
+                               "profiles/; reported only while the kernel's sources hash as "
+                               "they did then" if traffic is not None else
+                               "null: no counter passes of this kernel as it is now"),
             "avg_launch_us": round(s1["ms"] * 1e3, 2),
             "algorithmic_bytes_per_launch": int(s1["bytes"]),
         },
@@ -732,6 +749,7 @@ def main():
         "kernels_us": {k: round(v * 1e3, 2) for k, v in head["per_kernel_ms"].items()},
         "step_spread": head["spread"],
         "decode_sweep": sweep,
+        "decode_single_launch": single,
         "ep_share": ep,
         "prefill": prefill,
         "skewed_prefill": skewed,

@@ -33,6 +33,24 @@ class FP4MoEError(RuntimeError):
         self.status = status
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int), ("H", ctypes.c_int), ("I", ctypes.c_int), ("E", ctypes.c_int),
+        ("n_shared", ctypes.c_int), ("n_group", ctypes.c_int), ("topk_group", ctypes.c_int),
+        ("topk", ctypes.c_int), ("renormalize", ctypes.c_int), ("max_tiles", ctypes.c_int),
+        ("routed_scale", ctypes.c_float),
+        ("x", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+        ("w2_scale", ctypes.c_void_p),
+        ("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+        ("expert_offsets", ctypes.c_void_p), ("sorted_pairs", ctypes.c_void_p),
+        ("pair_pos", ctypes.c_void_p), ("tiles", ctypes.c_void_p), ("n_tiles", ctypes.c_void_p),
+        ("n_dropped", ctypes.c_void_p), ("h", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 class GemmArgs(ctypes.Structure):
     _fields_ = [
         ("stage", ctypes.c_int), ("wfmt", ctypes.c_int), ("afmt", ctypes.c_int),
@@ -79,6 +97,8 @@ def load():
         "moe_combine": ([P, P, P, I, I, I, I, P, P, P], I),
         "fp4_weight_preshuffle": ([I, I, I, I, P, P, P, P, P], I),
         "mxfp4_to_fp8_channel": ([P, P, I64, I, P, P, P, P, P], I),
+        "moe_decode_fused_workspace": ([I], S),
+        "moe_decode_fused": ([ctypes.POINTER(DecodeArgs), P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -392,4 +412,37 @@ def mxfp4_to_fp8_channel(codes, scales, fp8=None, channel_scale=None, row_status
     return fp8, channel_scale, row_status, n_inexact
 
 
+def moe_decode_fused(x, logits, bias, w13, w13_scale, w2, w2_scale, *, I, n_shared, n_group,
+                     topk_group, topk, workspace, out, renormalize=True, routed_scale=1.0,
+                     stream=None):
+    """The whole decode layer (T <= 16, bf16 activations, fragment-major MXFP4
+    weights) in one launch.  `out` holds the caller's buffers: topk_ids, topk_w,
+    perm (the dict moe_permute returns, tiles sized for block_m 16), h, y and
+    out.  `workspace`: moe_decode_fused_workspace(H) bytes, zero-filled before
+    the first call (uint8 or int32 tensor)."""
+    lib = load()
+    T, H = x.shape
+    E = logits.shape[1]
+    perm = out["perm"]
+    a = DecodeArgs(T=T, H=H, I=I, E=E, n_shared=n_shared, n_group=n_group,
+                   topk_group=topk_group, topk=topk, renormalize=int(bool(renormalize)),
+                   max_tiles=perm["tiles"].shape[0], routed_scale=float(routed_scale),
+                   x=x.data_ptr(), logits=logits.data_ptr(),
+                   bias=bias.data_ptr() if bias is not None else None,
+                   w13=w13.data_ptr(), w13_scale=w13_scale.data_ptr(), w2=w2.data_ptr(),
+                   w2_scale=w2_scale.data_ptr(),
+                   topk_ids=out["topk_ids"].data_ptr(), topk_w=out["topk_w"].data_ptr(),
+                   expert_offsets=perm["expert_offsets"].data_ptr(),
+                   sorted_pairs=perm["sorted_pairs"].data_ptr(),
+                   pair_pos=perm["pair_pos"].data_ptr(), tiles=perm["tiles"].data_ptr(),
+                   n_tiles=perm["n_tiles"].data_ptr(), n_dropped=perm["n_dropped"].data_ptr(),
+                   h=out["h"].data_ptr(), y=out["y"].data_ptr(), out=out["out"].data_ptr(),
+                   workspace=workspace.data_ptr(),
+                   workspace_bytes=workspace.numel() * workspace.element_size())
+    _check(lib.moe_decode_fused(ctypes.byref(a), _stream(stream)))
+    return out
+
+
+
 from .layer import MoELayer, LayerConfig  # noqa: E402,F401
+

@@ -130,8 +130,9 @@ __device__ __forceinline__ v8bf decode_nv8(uint32_t d, float scale) {
 
 // NVFP4 in f16: eight E2M1 values of dword `d` (element 2i in the low nibble
 // of byte i) times the E4M3 block scale given as a pair (sb, sb).  Both
-// factors and the product (at most 5 significant bits, 2^-10 .. 2688) are
-// exact in f16, so one conversion and one packed f16 multiply per pair.
+// factors and the product (at most 6 significant bits: 2 of E2M1 times 4 of
+// E4M3; magnitudes 2^-10 .. 2688) are exact in f16, so one conversion and one
+// packed f16 multiply per pair.
 __device__ __forceinline__ v8h decode_nv8_f16(uint32_t d, v2h sb2) {
   const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sb2;
   const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sb2;

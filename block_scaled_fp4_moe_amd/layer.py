@@ -6,8 +6,10 @@ decode sizes) -> activation quantization
 (mxfp4_quant_1x32 | nvfp4_qdq | none) -> fp4_grouped_gemm stage 1 (gate/up,
 SiLU*up) -> quantization of h (in the stage-1 epilogue for 192-row tiles) ->
 fp4_grouped_gemm stage 2 (down) ->
-moe_combine.  Every step is a kernel of libfp4moe; this module only
-allocates device buffers (once per token count) and passes pointers.
+moe_combine.  Decode batches of at most 16 tokens with bf16 activations and
+MXFP4 weights take all of it in one launch (moe_decode_fused) instead.
+Every step is a kernel of libfp4moe; this module only allocates device
+buffers (once per token count) and passes pointers.
 """
 
 from dataclasses import dataclass
@@ -16,9 +18,8 @@ import torch
 
 from . import (A_BF16, A_F16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
                LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle, moe_combine,
-               moe_permute, moe_permute_max_tiles, moe_route, moe_route_permute,
-               mxfp4_quant_1x32,
-               mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
+               moe_decode_fused, moe_permute, moe_permute_max_tiles, moe_route,
+               moe_route_permute, mxfp4_quant_1x32, mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
 
 
 # moe_route_permute (one launch, one workgroup) takes T * (topk + n_shared) up
@@ -26,6 +27,9 @@ from . import (A_BF16, A_F16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYO
 # about 8 tokens the two launches (one workgroup per token for the routing)
 # measured faster.
 ROUTE_PERMUTE_MAX_TOKENS = 8
+
+# moe_decode_fused (the whole layer in one launch) takes at most 16 tokens.
+FUSED_DECODE_MAX_TOKENS = 16
 
 
 @dataclass
@@ -43,6 +47,11 @@ class LayerConfig:
     renormalize: bool = True
     routed_scale: float = 1.0
     fragment_layout: bool = True   # stream weights from the fragment-major layout
+    # one launch (moe_decode_fused) where it applies; off by default: on
+    # MI355X its grid barrier and per-item release fences cost more than the
+    # kernel boundaries of the chain of calls (measured: T=1 275 us against
+    # 57 us, T=8 740 us against 194 us)
+    fused_decode: bool = False
 
 
 class MoELayer:
@@ -85,6 +94,16 @@ class MoELayer:
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
+        # the single-launch decode: bf16 activations, fragment-major MXFP4
+        # weights, 16-row tiles (its workspace is zero-filled once, here)
+        self.fused_ok = (cfg.fused_decode and cfg.afmt == "bf16" and cfg.wfmt == "mx" and
+                         cfg.fragment_layout and cfg.block_m == 16 and cfg.H % 128 == 0 and
+                         cfg.I % 128 == 0 and cfg.topk <= 16 and cfg.n_shared <= 8 and
+                         cfg.E + cfg.n_shared <= 1032)
+        self.fused_ws = None
+        if self.fused_ok:
+            nbytes = load().moe_decode_fused_workspace(cfg.H)
+            self.fused_ws = torch.zeros((nbytes + 3) // 4, dtype=torch.int32, device=device)
 
     def _buffers(self, T):
         if T in self._bufs:
@@ -140,6 +159,15 @@ class MoELayer:
         T = x.shape[0]
         k = c.topk + c.n_shared
         b = self._buffers(T)
+        if (self.fused_ok and 1 <= T <= FUSED_DECODE_MAX_TOKENS and logits.shape[1] == c.E):
+            tick("fused")
+            moe_decode_fused(x, logits, bias, self.w["w13"], self.w["w13_scale"], self.w["w2"],
+                             self.w["w2_scale"], I=c.I, n_shared=c.n_shared, n_group=c.n_group,
+                             topk_group=c.topk_group, topk=c.topk, workspace=self.fused_ws,
+                             out=b, renormalize=c.renormalize, routed_scale=c.routed_scale,
+                             stream=stream)
+            tick(None)
+            return b if keep else b["out"]
         # (one launch only when every routed expert is local: the fused call
         # permutes over the same E it routes over)
         if T <= ROUTE_PERMUTE_MAX_TOKENS and T * k <= 1024 and logits.shape[1] == c.E:

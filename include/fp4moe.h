@@ -265,7 +265,7 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * are not written.
  * afmt FP4MOE_A_F16 (the f16 operand form of nvfp4_qdq; a_f16_scale points
  * to its power-of-two factor) is taken with NVFP4 fragment-major weights and
- * block_m 64: E2M1 times E4M3 is exact in f16 (at most 5 significant bits,
+ * block_m 64: E2M1 times E4M3 is exact in f16 (at most 6 significant bits,
  * magnitudes 2^-10 .. 2688), so the products equal those of the bf16 form
  * and the factor is applied with the tensor scale in the epilogue.
  */
@@ -357,6 +357,62 @@ int fp4_weight_preshuffle(int wfmt, int E, int N, int K, const uint8_t* codes,
  */
 int moe_combine(const uint16_t* y_sorted, const int32_t* pair_pos, const float* topk_w, int T,
                 int topk, int n_shared, int H, uint16_t* out, float* out_f32, void* stream);
+
+/*
+ * moe_decode_fused -- the whole decode layer in one launch, for T <= 16
+ * tokens: bf16 activations, MXFP4 weights in the fragment-major layout of
+ * fp4_weight_preshuffle.
+ * [GAUDI] "What was built" (decode kernels for at most 16 tokens that touch
+ * only the routed experts); [ATOM] "Stage D: MXFP4 Fused MoE" (the
+ * small-token down GEMM that reduces the experts' rows into the tokens
+ * itself); [K3] "Copy inputs only for kernels that use them" (fixed
+ * per-launch costs dominate small steps).
+ * Computes exactly what moe_route_permute (block_m 16), fp4_grouped_gemm
+ * stage 1 and stage 2 (MXFP4 x bf16, block_m 16) and moe_combine compute with
+ * the same arguments, and writes the same outputs bit for bit: topk_ids
+ * [T, topk], topk_w [T, topk], expert_offsets [E+n_shared+1], sorted_pairs
+ * and pair_pos [T*k], tiles [max_tiles, 2] (max_tiles at least
+ * moe_permute_max_tiles(T, topk, E, n_shared, 16)), n_tiles [1], n_dropped
+ * [1], h bf16 [T*k, I] and y bf16 [T*k, H] in sorted order, out bf16 [T, H].
+ * All experts are local (ids index the weight tensors directly).
+ * Requires T <= 16, topk <= 16, n_shared <= 8, E + n_shared <= 1032, the
+ * routing limits of moe_route, H and I multiples of 128; x, the weights, h,
+ * y and out 16-byte aligned.
+ * workspace: moe_decode_fused_workspace(H) bytes of device memory, zero-filled
+ * by the caller before the first call; every completed call leaves it as a
+ * later call needs it (word 0 and words 4.. back at zero, word 1 advanced).
+ * Word 2 is a sticky flag the kernel sets if a wait at its grid barrier gave
+ * up (never in a correct run; the outputs are then invalid); the caller
+ * clears it.  The launch is cooperative (all workgroups resident at once) and
+ * returns FP4MOE_ERR_LAUNCH if the device cannot host it.  Calls sharing one
+ * workspace must not overlap.
+ */
+typedef struct {
+  int T, H, I, E, n_shared, n_group, topk_group, topk, renormalize, max_tiles;
+  float routed_scale;
+  const uint16_t* x;        /* bf16 [T, H]                                     */
+  const float* logits;      /* [T, E]                                          */
+  const float* bias;        /* [E] or NULL                                     */
+  const uint8_t* w13;       /* fragment-major MXFP4 [E+n_shared, 2I, H/2]      */
+  const uint8_t* w13_scale; /* fragment-major E8M0 [E+n_shared, 2I, H/32]      */
+  const uint8_t* w2;        /* fragment-major MXFP4 [E+n_shared, H, I/2]       */
+  const uint8_t* w2_scale;  /* fragment-major E8M0 [E+n_shared, H, I/32]       */
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* expert_offsets;
+  int32_t* sorted_pairs;
+  int32_t* pair_pos;
+  int32_t* tiles;
+  int32_t* n_tiles;
+  int32_t* n_dropped;
+  uint16_t* h;
+  uint16_t* y;
+  uint16_t* out;
+  void* workspace;
+  size_t workspace_bytes;
+} fp4moe_decode_args;
+size_t moe_decode_fused_workspace(int H);
+int moe_decode_fused(const fp4moe_decode_args* args, void* stream);
 
 /*
  * mxfp4_to_fp8_channel -- exact MXFP4 -> FP8 E4M3 per-channel conversion.

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
               "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked",
               "moe_route_permute", "mxfp4_linear"]:
@@ -235,3 +235,28 @@ def test_permute_noalloc_rejects_batches_beyond_its_buffer():
     st, msg = _status(lambda lib: lib.moe_permute_noalloc(p, T, topk, E, ns, bm, p, p, p, p, p, p,
                                                           None))
     assert st == 3 and "moe_permute_noalloc" in msg and "4194304" in msg
+
+
+def _decode_args(**kw):
+    a = fm.DecodeArgs(T=1, H=7168, I=2048, E=384, n_shared=1, n_group=8, topk_group=4, topk=8,
+                      renormalize=1, max_tiles=9, routed_scale=1.0)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("bad", [dict(T=17), dict(T=-1), dict(topk=17), dict(n_shared=9),
+                                 dict(H=7000), dict(I=2000), dict(E=1100), dict(n_group=5),
+                                 dict(max_tiles=8), dict(workspace_bytes=16)])
+def test_decode_fused_rejects_bad_arguments(bad):
+    """Argument and workspace checks of the single-launch decode, before any
+    device work (the pointers are never dereferenced)."""
+    lib = fm.load()
+    ws = lib.moe_decode_fused_workspace(7168)
+    assert ws == (4 + 112) * 4
+    a = _decode_args(**{"workspace_bytes": ws, **bad})
+    st, msg = _status(lambda lib: lib.moe_decode_fused(ctypes.byref(a), None))
+    assert st == 1 and "moe_decode_fused" in msg, (bad, st, msg)
+    # T = 0 with valid sizes is accepted and does nothing
+    a = _decode_args(T=0, max_tiles=0, workspace_bytes=ws)
+    assert _status(lambda lib: lib.moe_decode_fused(ctypes.byref(a), None))[0] == 0

@@ -1,6 +1,7 @@
 """Host-side behaviour of bench.py (no GPU needed): the refusals and the
 counter-derived traffic figure."""
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -34,16 +35,18 @@ def test_bench_without_gpu_fails_loudly():
     assert "needs an MI355X GPU" in r.stderr
 
 
-def test_stage1_traffic_only_for_the_counted_workload(monkeypatch):
+def test_roofline_traffic_only_for_the_counted_kernel_and_workload(monkeypatch):
+    """Stored counter bytes are reported only for the kernel and token count
+    they were taken on, and only while that kernel's sources are unchanged."""
     sys.path.insert(0, ROOT)
     import bench
-    assert bench.stage1_traffic(bench.STAGE1_COUNTERS["tokens"] + 1) is None
-    t = bench.stage1_traffic(bench.STAGE1_COUNTERS["tokens"])
-    if t is not None:
-        c = bench.STAGE1_COUNTERS
-        assert t == int((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
-    # a changed kernel source makes the stored counters stale
-    stale = dict(bench.STAGE1_COUNTERS)
-    stale["sha256"] = ("0" * 64,) + tuple(stale["sha256"][1:])
-    monkeypatch.setattr(bench, "STAGE1_COUNTERS", stale)
-    assert bench.stage1_traffic(stale["tokens"]) is None
+    src = "block_scaled_fp4_moe_amd/csrc/common.h"
+    sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    c = dict(tokens=8, fetch_kib=1000.0, write_kib=10.0, fetch_scale=2.0, write_scale=1.0,
+             sources=(src,), sha256=(sha,))
+    monkeypatch.setattr(bench, "ROOFLINE_COUNTERS", {"fused": c})
+    assert bench.roofline_traffic("fused", 8) == int((1000.0 * 2.0 + 10.0) * 1024)
+    assert bench.roofline_traffic("fused", 9) is None
+    assert bench.roofline_traffic("stage1", 8) is None
+    monkeypatch.setattr(bench, "ROOFLINE_COUNTERS", {"fused": dict(c, sha256=("0" * 64,))})
+    assert bench.roofline_traffic("fused", 8) is None

@@ -115,12 +115,12 @@ def _case(w, T, seed, afmt, wfmt):
     return _CASE
 
 
-def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, fragment=True):
+def run_layer(gpu_lib, w, T, afmt, wfmt, block_m, seed=0, fragment=True, fused=False):
     c = _case(w, T, seed, afmt, wfmt)
     logits, bias, xb, rid, rw, ref = c["logits"], c["bias"], c["xb"], c["rid"], c["rw"], c["ref"]
     cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                               topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
-                              block_m=block_m, fragment_layout=fragment)
+                              block_m=block_m, fragment_layout=fragment, fused_decode=fused)
     layer = gpu_lib.MoELayer(cfg, c["dev_w"])
     b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
     assert_equal(host(b["topk_ids"]), rid, "topk_ids")
@@ -171,9 +171,85 @@ def test_layer_empty_batch(gpu_lib, afmt, block_m):
     assert tuple(out.shape) == (0, H)
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
-def test_layer_decode_full_width(gpu_lib, T):
-    run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16)
+@pytest.mark.parametrize("T,fused", [(1, True), (8, True), (16, True), (1, False), (8, False),
+                                     (64, False)])
+def test_layer_decode_full_width(gpu_lib, T, fused):
+    """The decode layer at full width against the oracle: one launch
+    (moe_decode_fused, up to 16 tokens) or the chain of calls."""
+    run_layer(gpu_lib, synth.WORKLOADS["decode"], T, "bf16", "mx", 16, fused=fused)
+
+
+def _fused_and_chain(gpu_lib, w, T, seed):
+    """Outputs of the single-launch decode and of the chain of calls on the same
+    inputs, and the fused layer's workspace after its calls."""
+    c = _case(w, T, seed, "bf16", "mx")
+    outs = []
+    for fused in (True, False):
+        cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                                  topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx",
+                                  block_m=16, fused_decode=fused)
+        layer = gpu_lib.MoELayer(cfg, c["dev_w"])
+        if fused:
+            assert layer.fused_ok
+            ws = layer.fused_ws
+        b = layer.forward(bf16_dev(c["xb"]), dev(c["logits"]), dev(c["bias"]), keep=True)
+        n = int(host(b["perm"]["expert_offsets"])[-1])
+        nt = int(host(b["perm"]["n_tiles"])[0])
+        outs.append({k: host(b[k]).copy() for k in ("topk_ids", "topk_w")} |
+                    {k: host(b["perm"][k]).copy() for k in ("expert_offsets", "sorted_pairs",
+                                                             "pair_pos", "n_tiles", "n_dropped")} |
+                    {"tiles": host(b["perm"]["tiles"])[:nt].copy(),
+                     "h": bits_of(b["h"])[:n].copy(), "y": bits_of(b["y"])[:n].copy(),
+                     "out": bits_of(b["out"]).copy()})
+    return outs[0], outs[1], host(ws).copy(), c
+
+
+@pytest.mark.parametrize("wname,T", [("decode", 1), ("decode", 2), ("decode", 5), ("decode", 16),
+                                     ("tiny", 1), ("tiny", 16)])
+def test_decode_fused_matches_chain_bit_for_bit(gpu_lib, wname, T):
+    """moe_decode_fused writes exactly what route+permute, both dq stages and
+    the combine write (every output byte), the outputs match the oracle, and
+    the workspace is back to its reusable state (counters at zero, no barrier
+    timeout)."""
+    w = synth.WORKLOADS[wname]
+    f, u, ws, c = _fused_and_chain(gpu_lib, w, T, 0)
+    for key in u:
+        assert f[key].shape == u[key].shape and f[key].tobytes() == u[key].tobytes(), \
+            f"{key}: fused and chained outputs differ"
+    assert ws[0] == 0 and ws[2] == 0 and not ws[4:].any(), ws[:8]
+    ref = c["ref"]
+    assert_equal(f["topk_ids"], c["rid"], "topk_ids")
+    assert_equal(f["pair_pos"], ref["perm"]["pair_pos"], "pair_pos")
+    assert_bf16_close(f["out"], ref["out"], "out")
+
+
+def test_decode_fused_repeated_calls(gpu_lib):
+    """Many calls in a row on changing inputs: each equals the chain, and the
+    barrier generation word advances once per call."""
+    w = synth.WORKLOADS["decode"]
+    cfg = gpu_lib.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                              topk_group=w.topk_group, topk=w.topk, afmt="bf16", wfmt="mx",
+                              block_m=16, fused_decode=True)
+    ref_cfg = gpu_lib.LayerConfig(**{**cfg.__dict__, "fused_decode": False})
+    T = 8
+    c = _case(w, T, 0, "bf16", "mx")
+    fused = gpu_lib.MoELayer(cfg, c["dev_w"])
+    chain = gpu_lib.MoELayer(ref_cfg, c["dev_w"])
+    g0 = int(host(fused.fused_ws)[1])
+    bias = dev(c["bias"])
+    rng = np.random.default_rng(7)
+    for i in range(12):
+        # same experts as the case (their weights are the only ones written):
+        # permute the tokens and scale the logits of the routed experts up
+        perm_t = rng.permutation(T)
+        xb = c["xb"][perm_t]
+        lg = c["logits"][perm_t].copy()
+        x_d, l_d = bf16_dev(xb), dev(lg)
+        a = bits_of(fused.forward(x_d, l_d, bias)).copy()
+        b = bits_of(chain.forward(x_d, l_d, bias)).copy()
+        assert a.tobytes() == b.tobytes(), f"call {i}"
+    ws = host(fused.fused_ws)
+    assert int(ws[1]) - g0 == 12 and ws[0] == 0 and ws[2] == 0 and not ws[4:].any()
 
 
 def test_layer_decode_is_deterministic(gpu_lib):
