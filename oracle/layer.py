@@ -11,6 +11,8 @@ Activation paths:
   bf16   activations enter the GEMM as bf16 (weights dequantized in the tile)
   mx     activations are quantized with mxfp4_quant_1x32 before each GEMM
   nvfp4  activations pass the NVFP4 QDQ round trip before each GEMM
+  fp8    activations are quantized to FP8 E4M3 per row (per token before
+         stage 1, per sorted row of h before stage 2) before each GEMM
 
 `weights` maps names to per-expert indexable arrays:
   w13, w13_scale, w2, w2_scale and, for nvfp4, w13_ts / w2_ts (float32 [E]).
@@ -36,6 +38,8 @@ def activation_values(afmt, x_bits):
         if x_bits.shape[0] == 0:
             return np.zeros(x_bits.shape)
         return F.bf16_decode(Q.nvfp4_qdq(x_bits)["y"])
+    if afmt == "fp8":
+        return Q.fp8_qdq_values(x_bits)
     raise ValueError(afmt)
 
 

@@ -12,6 +12,16 @@ pages give no scale rule or rounding mode.  Reading (the OCP MX rule):
   3. each element becomes the E2M1 code nearest to x / 2^e, ties to even,
      saturating at +-6, keeping the sign (so small negatives give code 0x8).
 
+fp8_quant_per_token -- [GAUDI] "Exact MXFP4 to FP8 per-channel conversion":
+the converted FP8 experts are served with per-channel weight scales and
+dynamic per-token FP8 activations (W8A8).  The page gives no scale rule.
+Reading (the plain dynamic per-row rule), in IEEE float32 like nvfp4_qdq:
+  1. s_r = amax_r / 448 over the row (448 = largest OCP E4M3FN magnitude);
+     s_r = 1 when the row is all zero.
+  2. code = E4M3(x / s_r): one float32 division, then round to nearest even,
+     saturating at +-448, sign kept.
+  3. the value the GEMM sees is decode(code) * s_r (exact in float64).
+
 nvfp4_qdq -- [NVFP4] "Weight Dequantization and Activation QDQ": activations
 pass through an NVFP4 quantize-dequantize round trip before each GEMM.  The
 page fixes no arithmetic.  Reading, every step an IEEE float32 operation
@@ -29,6 +39,7 @@ import numpy as np
 from . import formats as F
 
 E2M1_EMAX = 2   # exponent of the largest E2M1 magnitude, 6 = 1.5 * 2^2
+FP8_MAX = 448.0  # largest OCP E4M3FN magnitude
 
 
 def mxfp4_quant_1x32(x_bits):
@@ -81,3 +92,20 @@ def nvfp4_qdq(x_bits, tensor_scale_in=None):
     y = F.bf16_bits(yv.astype(np.float64)).reshape(M, K)
     return dict(y=y, codes=F.pack_fp4(codes.reshape(M, K)), scales=sb_codes,
                 tensor_scale=float(s_t))
+
+
+def fp8_quant_per_token(x_bits):
+    """bf16 bit patterns [M, K] -> (E4M3 codes uint8 [M, K], scales float32 [M])."""
+    f32 = np.float32
+    x = F.bf16_decode(x_bits).astype(np.float32)     # exact
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    s = np.where(amax > 0, (amax / f32(FP8_MAX)).astype(np.float32), f32(1.0)).astype(np.float32)
+    q = (x / s[:, None]).astype(np.float32)          # float32 division
+    return F.e4m3_encode(q.astype(np.float64)), s
+
+
+def fp8_qdq_values(x_bits):
+    """Values the W8A8 path feeds the GEMM: decode(code) * s_r, float64 [M, K]."""
+    codes, s = fp8_quant_per_token(x_bits)
+    return F.e4m3_decode(codes) * s.astype(np.float64)[:, None]
+

@@ -150,6 +150,14 @@ def _chain_weights(wfmt, Et, H, I, seed):
     g = np.random.default_rng(seed)
     if wfmt == "mx":
         return _tiny_weights(Et, H, I, seed)
+    if wfmt == "fp8":
+        w = {}
+        for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
+            c = g.integers(0, 256, (Et, N, K), dtype=np.uint8)
+            c[(c & 0x7F) == 0x7F] = 0x38
+            w[name] = c
+            w[name + "_scale"] = np.ldexp(1.0, g.integers(-6, -2, (Et, N))).astype(np.float32)
+        return w
     w = {}
     for name, (N, K) in (("w13", (2 * I, H)), ("w2", (H, I))):
         w[name] = g.integers(0, 256, (Et, N, K // 2), dtype=np.uint8)
@@ -168,11 +176,15 @@ def _chain_brute_force(xb, ids, wts, w, afmt, wfmt, E, n_shared, I, requant_h=Tr
     def weight(name, e):
         if wfmt == "mx":
             return F.mxfp4_dequant(w[name][e], w[name + "_scale"][e])
+        if wfmt == "fp8":
+            return F.e4m3_decode(w[name][e]) * w[name + "_scale"][e].astype(np.float64)[:, None]
         return F.nvfp4_dequant(w[name][e], w[name + "_scale"][e], w[name + "_ts"][e])
 
     def qdq_rows(rows_bits, s_t=None):
         if afmt == "mx":
             return [Q.mxfp4_qdq_values(r[None])[0] for r in rows_bits]
+        if afmt == "fp8":
+            return [Q.fp8_qdq_values(r[None])[0] for r in rows_bits]
         return [F.bf16_decode(Q.nvfp4_qdq(r[None], tensor_scale_in=s_t)["y"])[0]
                 for r in rows_bits]
 
@@ -226,3 +238,9 @@ def test_layer_mx_activation_chain_brute_force():
 
 def test_layer_nvfp4_activation_chain_brute_force():
     _check_chain("nvfp4", "nvfp4", 42)
+
+
+def test_layer_fp8_activation_chain_brute_force():
+    """W8A8: per-token FP8 activations before stage 1, per-row FP8 of h before
+    stage 2, FP8 weights with per-channel scales."""
+    _check_chain("fp8", "fp8", 44)

@@ -27,6 +27,17 @@ _orig_floor = OF.floor_log2
 _orig_round = OF.round_to_grid
 _orig_silu = OG.silu_mul
 _orig_act = OL.activation_values
+_orig_fp8q = OQ.fp8_quant_per_token
+
+
+def _fp8_scale_per_tensor(x_bits):
+    """The per-token FP8 rule with one scale for the whole tensor."""
+    codes, s = _orig_fp8q(x_bits)
+    x = OF.bf16_decode(x_bits).astype(np.float32)
+    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    st = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    q = (x / st).astype(np.float32)
+    return OF.e4m3_encode(q.astype(np.float64)), np.full(x.shape[0], st, np.float32)
 
 
 def _nvfp4_scale_per_row(afmt, x_bits):
@@ -75,6 +86,8 @@ MUTANTS = {
                                            lambda afmt, h, h_bits, rounding=True:
                                            OF.bf16_decode(h_bits) if rounding else h)],
     "NVFP4 tensor scale per row": [(OL, "activation_values", _nvfp4_scale_per_row)],
+    "FP8 activation scale per tensor, not per token": [(OQ, "fp8_quant_per_token",
+                                                        _fp8_scale_per_tensor)],
     "gate/up swapped": [(OG, "silu_mul", lambda gu, I: _orig_silu(
         np.concatenate([gu[:, I:], gu[:, :I]], axis=1), I))],
 }

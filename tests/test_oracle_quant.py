@@ -125,3 +125,59 @@ def test_nvfp4_codes_brute_force_dynamic():
 def test_nvfp4_zero_tensor():
     r = Q.nvfp4_qdq(np.zeros((2, 32), dtype=np.uint16))
     assert r["tensor_scale"] == 1.0 and np.all(r["y"] == 0) and np.all(r["scales"] == 0)
+
+
+# --------------------------------------------------------------------------
+# Dynamic per-token FP8 (the W8A8 activations)
+# --------------------------------------------------------------------------
+
+def _e4m3_table():
+    """Every finite OCP E4M3FN code and its value, from the bit fields."""
+    out = []
+    for c in range(256):
+        if (c & 0x7F) == 0x7F:
+            continue
+        e, m = (c >> 3) & 15, c & 7
+        v = (m / 8) * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        out.append((c, -v if c & 0x80 else v))
+    return out
+
+
+def _nearest_e4m3_code(q):
+    """Brute force: nearest finite value (saturating), ties to the even mantissa, sign kept."""
+    tab = [(c, v) for c, v in _e4m3_table() if (c & 0x80) == (0x80 if np.signbit(q) else 0)]
+    a = min(abs(q), 448.0)
+    d = [abs(abs(v) - a) for _, v in tab]
+    best = [c for (c, _), di in zip(tab, d) if di == min(d)]
+    if len(best) > 1:
+        best = [c for c in best if c % 2 == 0]
+    return best[0]
+
+
+def test_fp8_per_token_scale_and_codes_brute_force():
+    g = np.random.default_rng(21)
+    x = g.standard_normal((6, 40)) * np.exp(g.uniform(-8, 8, (6, 1)))
+    x[2, 5] = 0.0
+    xb = _bf16(x)
+    codes, s = Q.fp8_quant_per_token(xb)
+    xv = F.bf16_decode(xb).astype(np.float32)
+    for r in range(6):
+        amax = np.float32(np.abs(xv[r]).max())
+        assert s[r] == np.float32(amax / np.float32(448.0))
+        for i in range(40):
+            q = float(np.float32(xv[r, i] / s[r]))
+            assert codes[r, i] == _nearest_e4m3_code(q), (r, i, q)
+        # the row maximum lands on +-448
+        i = int(np.argmax(np.abs(xv[r])))
+        assert codes[r, i] & 0x7F == 0x7E
+
+
+def test_fp8_per_token_hand_example_and_zero_row():
+    xb = _bf16([[1.0, -2.0, 0.5, 0.0], [0.0, -0.0, 0.0, 0.0]])
+    codes, s = Q.fp8_quant_per_token(xb)
+    assert s[0] == np.float32(np.float32(2.0) / np.float32(448.0)) and s[1] == 1.0
+    # 1 / s = 224 = 1.75 * 2^7, 2 / s = 448, 0.5 / s = 112 = 1.75 * 2^6
+    assert codes[0].tolist() == [0x76, 0xFE, 0x6E, 0x00]
+    assert codes[1].tolist() == [0x00, 0x80, 0x00, 0x00]
+    v = Q.fp8_qdq_values(xb)
+    assert v[0, 1] == -448.0 * float(s[0]) and v[1].tolist() == [0.0, -0.0, 0.0, 0.0]
