@@ -471,7 +471,25 @@ def run_fp8(fm, steps, torch, args):
                         workload=f"FP8-weight MoE layer, T={w.T}, Zipf(1.1) routing, converted "
                                  "E4M3 weights x MXFP4 activations on the gfx950 scaled MFMA "
                                  f"(FP4 x FP8, block_m {FP8_BLOCK_M})")
+    # W8A8: the same converted experts with dynamic per-token FP8 activations
+    cfg8 = fm.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
+                          topk_group=w.topk_group, topk=w.topk, afmt="fp8", wfmt="fp8",
+                          block_m=128)
+    layer8 = fm.MoELayer(cfg8, layer.w, preshuffled=True)
     del layer
+    torch.cuda.empty_cache()
+    r = time_layer(layer8, batches, bias, steps, 1, torch)
+    tflops = FLOP_PER_PAIR * w.T * (w.topk + w.n_shared) / (r["ms_per_step"] * 1e-3) / 1e12
+    log(args, f"w8a8 layer T={w.T}: {r['ms_per_step']:.3f} ms/step, {tflops:.0f} TFLOP/s, "
+              "kernels(ms)=" + json.dumps({k2: round(v, 3) for k2, v in r['per_kernel_ms'].items()}))
+    res["w8a8_layer"] = dict(tflops=round(tflops, 1), ms_per_step=round(r["ms_per_step"], 3),
+                             frac_of_fp8_peak=round(tflops / FP8_PEAK_TFLOPS, 4),
+                             kernels_ms={k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
+                             workload=f"W8A8 MoE layer, T={w.T}, Zipf(1.1) routing, converted "
+                                      "E4M3 weights (per-channel scales) x dynamic per-token FP8 "
+                                      "activations (fp8_quant_per_token) on the gfx950 scaled "
+                                      "MFMA (FP8 x FP8, block_m 128)")
+    del layer8
     torch.cuda.empty_cache()
     return res
 

@@ -6,8 +6,9 @@ functions take and return torch tensors.  There is no fallback: if the
 library is not built or the device is not gfx950, calls raise.
 
 Entry points (same names as the C ABI): moe_route, moe_permute,
-mxfp4_quant_1x32, nvfp4_qdq, fp4_grouped_gemm, moe_combine,
-mxfp4_to_fp8_channel.  `MoELayer` (layer.py) chains them into the layer.
+mxfp4_quant_1x32, nvfp4_qdq, fp8_quant_per_token, fp4_grouped_gemm,
+moe_combine, mxfp4_to_fp8_channel, moe_decode_fused, and the helpers the
+header declares.  `MoELayer` (layer.py) chains them into the layer.
 """
 
 import ctypes
@@ -19,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfp4moe.so")
 
 W_MXFP4, W_NVFP4, W_FP8 = 0, 1, 2
-A_BF16, A_MXFP4, A_F16 = 0, 1, 2
+A_BF16, A_MXFP4, A_F16, A_FP8 = 0, 1, 2, 3
 LAYOUT_ROWMAJOR, LAYOUT_FRAGMENT = 0, 1
 A_LAYOUT_ROWMAJOR, A_LAYOUT_CHUNKED = 0, 1
 WFMT = {"mx": W_MXFP4, "nvfp4": W_NVFP4, "fp8": W_FP8}
@@ -65,7 +66,7 @@ class GemmArgs(ctypes.Structure):
         ("out", ctypes.c_void_p), ("ldo", ctypes.c_int64), ("out_f32", ctypes.c_void_p),
         ("w_layout", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_int),
         ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p), ("out_q_rows", ctypes.c_int),
-        ("a_f16_scale", ctypes.c_void_p),
+        ("a_f16_scale", ctypes.c_void_p), ("a_row_scale", ctypes.c_void_p),
     ]
 
 
@@ -90,6 +91,7 @@ def load():
         "moe_route_permute": ([P, P, I, I, I, I, I, I, F, I, I, P, P, P, P, P, P, P, P, P], I),
         "mxfp4_quant_1x32": ([P, I, I, I64, P, P, P, P, P], I),
         "mxfp4_quant_1x32_chunked": ([P, I, I, I64, P, I, I, P, P, P, P], I),
+        "fp8_quant_per_token": ([P, I, I, I64, P, I, P, P, P], I),
         "nvfp4_qdq_workspace": ([], S),
         "nvfp4_qdq": ([P, I, I, P, P, P, P, P, P, P, P, P, S, P], I),
         "fp4_grouped_gemm": ([ctypes.POINTER(GemmArgs), P], I),
@@ -292,7 +294,7 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
                      gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
                      a_layout=0, out_q=None, out_q_scale=None, no_out=False, a_f16_scale=None,
-                     stream=None):
+                     a_row_scale=None, stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
@@ -300,6 +302,8 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
     MXFP4 codes [K/128, rows, 64] with a_scale [K/128, rows, 4] (a_layout 1).
     afmt A_F16: a is the f16 operand form of nvfp4_qdq (viewed as int16 / float16)
     and a_f16_scale its float32 [1] power-of-two factor.
+    afmt A_FP8 (FP8 weights, block_m 128): a is fp8_quant_per_token's chunk-major
+    E4M3 codes [K/128, rows, 128] and a_row_scale its float32 [rows] scales.
     out_q / out_q_scale (stage 1, block_m 192): chunk-major MXFP4 copies of the
     output [N_out/128, rows, 64] / [N_out/128, rows, 4]; with no_out=True the
     bf16 output is not written (returns None).
@@ -336,9 +340,26 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     None if out_q is None else out_q.data_ptr(),
                     None if out_q_scale is None else out_q_scale.data_ptr(),
                     0 if out_q is None else out_q.shape[1],
-                    None if a_f16_scale is None else a_f16_scale.data_ptr())
+                    None if a_f16_scale is None else a_f16_scale.data_ptr(),
+                    None if a_row_scale is None else a_row_scale.data_ptr())
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
+
+
+def fp8_quant_per_token(x, row_count=None, out_rows=None, codes=None, scales=None, stream=None):
+    """Dynamic per-token FP8 of bf16 rows x [M, K]: codes chunk-major
+    [K/128, out_rows, 128] (uint8 E4M3) and scales float32 [out_rows]."""
+    lib = load()
+    M, K = x.shape
+    out_rows = M if out_rows is None else out_rows
+    if codes is None:
+        codes = torch.empty((K // 128, out_rows, 128), dtype=torch.uint8, device=_dev(x))
+    if scales is None:
+        scales = torch.empty(out_rows, dtype=torch.float32, device=_dev(x))
+    x_ = _u16(x)
+    _check(lib.fp8_quant_per_token(_p(x_), M, K, x_.stride(0), _p(row_count), out_rows,
+                                   _p(codes), _p(scales), _stream(stream)))
+    return codes, scales
 
 
 def mxfp4_linear(a, a_scale, w, w_scale, a_layout=0, M=None, out=None, out_f32=None,

@@ -35,10 +35,17 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   const bool mx = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_MXFP4;
   // FP8 weights x MXFP4 activations on the scaled MFMA: 192-row tiles
   const bool mx8 = a->afmt == FP4MOE_A_MXFP4 && a->wfmt == FP4MOE_W_FP8 && a->block_m == 192;
-  const bool dq = !mx && !mx8;
+  // FP8 weights x FP8 activations (W8A8): 128-row tiles on the scaled MFMA
+  const bool f8f8 = a->afmt == FP4MOE_A_FP8;
+  const bool dq = !mx && !mx8 && !f8f8;
   FP4MOE_REQUIRE(a->afmt == FP4MOE_A_BF16 || a->afmt == FP4MOE_A_MXFP4 ||
-                     a->afmt == FP4MOE_A_F16,
+                     a->afmt == FP4MOE_A_F16 || a->afmt == FP4MOE_A_FP8,
                  "fp4_grouped_gemm: afmt=%d", a->afmt);
+  FP4MOE_REQUIRE(!f8f8 || (a->wfmt == FP4MOE_W_FP8 && a->block_m == 128 &&
+                           a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
+                           a->a_layout == FP4MOE_A_LAYOUT_CHUNKED),
+                 "fp4_grouped_gemm: FP8 activations need FP8 fragment-major weights, block_m "
+                 "128 and chunk-major activations");
   FP4MOE_REQUIRE(a->wfmt == FP4MOE_W_MXFP4 || a->wfmt == FP4MOE_W_NVFP4 || a->wfmt == FP4MOE_W_FP8,
                  "fp4_grouped_gemm: wfmt=%d", a->wfmt);
   FP4MOE_REQUIRE(!(a->wfmt == FP4MOE_W_NVFP4 && a->afmt == FP4MOE_A_MXFP4),
@@ -60,9 +67,9 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
     FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64,
                    "fp4_grouped_gemm: block_m=%d not in {16,32,64} for this format pair",
                    a->block_m);
-  } else if (mx8) {
+  } else if (mx8 || f8f8) {
     FP4MOE_REQUIRE(a->w_layout == FP4MOE_LAYOUT_FRAGMENT,
-                   "fp4_grouped_gemm: block_m 192 needs fragment-major weights");
+                   "fp4_grouped_gemm: block_m %d needs fragment-major weights", a->block_m);
     const int n_out = a->stage == 1 ? a->N / 2 : a->N;
     const int out_per_wg = a->stage == 1 ? 128 : 256;
     FP4MOE_REQUIRE(n_out % out_per_wg == 0,
@@ -91,7 +98,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a->a_layout == FP4MOE_A_LAYOUT_ROWMAJOR || a->a_layout == FP4MOE_A_LAYOUT_CHUNKED,
                  "fp4_grouped_gemm: a_layout=%d", a->a_layout);
   const bool a_chunked = a->a_layout == FP4MOE_A_LAYOUT_CHUNKED;
-  FP4MOE_REQUIRE(!a_chunked || mx8 ||
+  FP4MOE_REQUIRE(!a_chunked || mx8 || f8f8 ||
                      (mx && a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
                       (a->block_m == 128 || a->block_m == 192 || a->block_m == 256)),
                  "fp4_grouped_gemm: chunked activations need MXFP4 activations, fragment "
@@ -110,10 +117,15 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   const int n_out = a->stage == 1 ? a->N / 2 : a->N;
   FP4MOE_REQUIRE(a->ldo >= n_out, "fp4_grouped_gemm: ldo=%lld < %d", (long long)a->ldo, n_out);
   // the 192-row tiles store 16-byte pieces of output rows
-  FP4MOE_REQUIRE(a->block_m != 192 || (a->ldo % 8 == 0 && ((uintptr_t)a->out & 15) == 0),
-                 "fp4_grouped_gemm: block_m 192 needs ldo %% 8 == 0 and a 16-byte aligned out");
+  FP4MOE_REQUIRE((a->block_m != 192 && !f8f8) ||
+                     (a->ldo % 8 == 0 && ((uintptr_t)a->out & 15) == 0),
+                 "fp4_grouped_gemm: block_m %d needs ldo %% 8 == 0 and a 16-byte aligned out",
+                 a->block_m);
   FP4MOE_REQUIRE(a_chunked || (a->lda >= a->K && a->lda % 32 == 0), "fp4_grouped_gemm: lda=%lld",
                  (long long)a->lda);
+  // the FP8 activation slab is addressed with 32-bit offsets within a K chunk
+  FP4MOE_REQUIRE(!f8f8 || (int64_t)a->a_rows * 128 <= (int64_t)0xffffffff,
+                 "fp4_grouped_gemm: a_rows=%d too large for FP8 activations", a->a_rows);
   const bool quant_out = a->out_q != nullptr || a->out_q_scale != nullptr;
   FP4MOE_REQUIRE(!quant_out || (a->out_q && a->out_q_scale && a->stage == 1 && a->block_m == 192 &&
                                 a->afmt == FP4MOE_A_MXFP4 && !a->out_f32 &&
@@ -136,6 +148,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a->afmt != FP4MOE_A_MXFP4 || a->a_scale,
                  "fp4_grouped_gemm: MXFP4 activations need a_scale");
   FP4MOE_REQUIRE(!f16a || a->a_f16_scale, "fp4_grouped_gemm: f16 activations need a_f16_scale");
+  FP4MOE_REQUIRE(!f8f8 || a->a_row_scale, "fp4_grouped_gemm: FP8 activations need a_row_scale");
   FP4MOE_REQUIRE(((uintptr_t)a->w & 15) == 0 && ((uintptr_t)a->a & 15) == 0,
                  "fp4_grouped_gemm: w and a must be 16-byte aligned");
   FP4MOE_CHECK_DEVICE();
@@ -167,11 +180,13 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   p.q_scales = a->out_q_scale;
   p.q_rows = a->out_q_rows;
   p.a_f16_scale = a->a_f16_scale;
+  p.a_row_scale = a->a_row_scale;
   hipStream_t s = as_stream(stream);
   const int mt = a->max_tiles;
   const int st = a->stage;
   if (mx) launch_mx_gemm(p, st, mt, s);
   else if (mx8) launch_mx_fp8_wide_gemm(p, st, mt, s);
+  else if (f8f8) launch_fp8_fp8_wide_gemm(p, st, mt, s);
   else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");

@@ -32,6 +32,9 @@
 //       whose operands are staged through LDS (gemm_dqt.hip).
 //   mx  (afmt MXFP4; wfmt MXFP4): v_mfma_scale_f32_*_f8f6f4 FP4 x FP4 with the
 //       E8M0 bytes as the scale operands (gemm_mx.hip), up to 192 x 512 tiles.
+//   f8f8 (afmt FP8; wfmt FP8; block_m 128): W8A8, the same kernel with E4M3
+//       activations (one float scale per row) against E4M3 weights, both MFMA
+//       format 0, 128 x 256 tiles; row and channel scales in the epilogue.
 //   mx8 (afmt MXFP4; wfmt FP8; block_m 192): the 192-row scaled-MFMA tiles of
 //       the mx family in the FP4 x FP8 form, E4M3 weights as MFMA format 0.
 //       Only the 32x32x64 form is used: in the 16x16x128 form each FP4 lane
@@ -79,6 +82,7 @@ struct GemmParams {
   int q_rows;
   const float* a_f16_scale;   // FP4MOE_A_F16: the activations' power-of-two factor
   int dense_rows;             // > 0: one dense matrix of this many rows, no tile list
+  const float* a_row_scale;   // FP4MOE_A_FP8: one float scale per activation row
 };
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -212,6 +216,9 @@ void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s
 void launch_mx_dense_gemm(const GemmParams& p, hipStream_t s);
 // FP8 weights x MXFP4 activations on the scaled MFMA (block_m 192, fragment weights).
 void launch_mx_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+// FP8 weights x per-row FP8 activations (W8A8, block_m 128, fragment weights,
+// chunk-major activations).
+void launch_fp8_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
 // Tiled dq variant (64-row tiles, fragment weights): whether it takes `p`.
 bool dqt_supported(const GemmParams& p, int stage);
 void launch_dqt_gemm(const GemmParams& p, int wfmt, int afmt, int stage, int max_tiles,

@@ -682,18 +682,28 @@ __device__ __forceinline__ void dma_b32_s(const void* base, uint32_t voff, uint3
                :: "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-template <int STAGE, bool W8>
+// A8 (with W8): W8A8, FP8 E4M3 activations with one float scale per row
+// (fp8_quant_per_token, chunk-major) against the FP8 weight fragments, both
+// MFMA format 0 with unit block scales; the row and channel scales multiply
+// the accumulators in the epilogue.  A 16-row activation block of a chunk is
+// laid out in LDS exactly like a weight fragment (2 KiB, the two 16-value
+// halves of every 32-value block 1 KiB apart), so the two operands pair K
+// the same way.  Tiles are 128 x 256 (a stage holds 16 KiB of activations
+// and 32 KiB of weights; three 192-row stages would not fit the LDS), each
+// wave 64 x 64 as 2 x 2 MFMA tiles; 6 DMA instructions per wave per chunk.
+template <int STAGE, bool W8, bool A8 = false>
 __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) {
-  constexpr int S = 3, NW = 8, BM = 192;
-  constexpr int WM = 6, MT = 3;                     // 16-row blocks / 32-row tiles per wave
+  static_assert(!A8 || W8, "FP8 activations run against FP8 weights");
+  constexpr int S = 3, NW = 8, BM = A8 ? 128 : 192;
+  constexpr int WM = BM / 32, MT = BM / 64;         // 16-row blocks / 32-row tiles per wave
   constexpr int WN = W8 ? 4 : 8, NT = WN / 2;       // weight groups / 32-row tiles per wave
   constexpr int NG_WG = 4 * WN;                     // weight groups per workgroup
   constexpr int GPW = NG_WG / NW;                   // weight groups copied per wave
   constexpr int GB = W8 ? 2048 : 1024;              // bytes of one weight fragment
   constexpr int OUT_PER_WAVE = (STAGE == 1) ? (WN / 2) * 16 : WN * 16;
   constexpr int OUT_PER_WG = 4 * OUT_PER_WAVE;
-  constexpr int OFF_AS = BM * 64;                   // A codes: [12 blocks][64 lanes][16 B]
-  constexpr int OFF_B = OFF_AS + BM * 4;            // A scales: [row][4 blocks]
+  constexpr int OFF_AS = BM * (A8 ? 128 : 64);      // A codes: [blocks][64 lanes][16 B] (A8: [blocks][2 KiB])
+  constexpr int OFF_B = OFF_AS + (A8 ? 0 : BM * 4); // A scales: [row][4 blocks] (none for A8)
   constexpr int OFF_BS = OFF_B + NG_WG * GB;        // B fragments: [NG_WG groups][GB]
   constexpr int STAGE_BYTES = OFF_BS + (W8 ? 0 : NW * 256);   // B scales: [8 waves][4 groups][64 B]
   constexpr int D = 2 + GPW * (GB / 1024) + (W8 ? 0 : 1);    // DMA instructions per wave per chunk
@@ -721,8 +731,8 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   const int64_t n_work = n_tiles_all * n_nb;
   const uint8_t* A = static_cast<const uint8_t*>(p.a);
   const bool chunked = p.a_layout == FP4MOE_A_LAYOUT_CHUNKED;
-  const int64_t a_row_bytes = chunked ? 64 : p.lda / 2, a_srow = chunked ? 4 : p.lda / 32;
-  const int64_t a_cstride = chunked ? (int64_t)p.a_rows * 64 : 64;
+  const int64_t a_row_bytes = A8 ? 128 : (chunked ? 64 : p.lda / 2), a_srow = chunked ? 4 : p.lda / 32;
+  const int64_t a_cstride = A8 ? (int64_t)p.a_rows * 128 : (chunked ? (int64_t)p.a_rows * 64 : 64);
   const int64_t as_cstride = chunked ? (int64_t)p.a_rows * 4 : 4;
   const uint32_t smem_base = lds_offset(smem);
 
@@ -737,7 +747,8 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   // fragment (l % 32) / 16 at lane' l % 16 + 16 * (2h + l / 32)
   const int m16 = (lane & 31) >> 4, kb = lane >> 5;
   const int frag_lane = m16 * 1024 + (lane & 15) * 16 + kb * 256;
-  const int a_lds = wm * WM * 1024 + frag_lane;
+  const int a_lds = A8 ? (wm * WM + m16) * 2048 + (lane & 15) * 16 + kb * 1024
+                      : wm * WM * 1024 + frag_lane;
   const int as_lds = OFF_AS + wm * WM * 64 + (lane & 31) * 4 + kb;
   // E4M3 operands of the 32x32x64 MFMA pair with E2M1 ones differently (read
   // on the device): with lane half kb of the E2M1 operand holding 32-value
@@ -764,9 +775,10 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       return p.gather ? (int64_t)(p.gather[r] / p.gather_div) : (int64_t)r;
     };
     // activation copies of this wave: fragments f0 (and f0+1 for waves 0-3),
-    // waves 4-7 also one 64-row scale block
-    const int f0 = grp == 0 ? 2 * wave : wave + 4;
-    const uint32_t a_off0 = (uint32_t)(src_row(tile_row0 + f0 * 16 + r16) * a_row_bytes) + g * 16;
+    // waves 4-7 also one 64-row scale block; A8: both halves of 16-row block
+    // `wave` (lane l: row l % 16, the 16-byte half of 32-value block l / 16)
+    const int f0 = A8 ? wave : (grp == 0 ? 2 * wave : wave + 4);
+    const uint32_t a_off0 = (uint32_t)(src_row(tile_row0 + f0 * 16 + r16) * a_row_bytes) + g * (A8 ? 32 : 16);
     const uint32_t a_off1 = (uint32_t)(src_row(tile_row0 + (f0 + 1) * 16 + r16) * a_row_bytes) + g * 16;
     const int sblk = grp == 0 ? 0 : min(wave - 4, 2);
     const uint32_t as_off = (uint32_t)(src_row(tile_row0 + sblk * 64 + lane) * a_srow);
@@ -785,7 +797,10 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
     auto issue = [&](int c) {
       const uint32_t st = smem_base + (uint32_t)((c % S) * STAGE_BYTES);
       const uint8_t* a_c = A + (int64_t)c * a_cstride;
-      if (grp == 0) {
+      if (A8) {
+        dma_b128_s(a_c, a_off0, st + f0 * 2048);
+        dma_b128_s(a_c, a_off0 + 16, st + f0 * 2048 + 1024);
+      } else if (grp == 0) {
         dma_b128_s(a_c, a_off0, st + f0 * 1024);
         dma_b128_s(a_c, a_off1, st + (f0 + 1) * 1024);
       } else {
@@ -809,8 +824,9 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[i][j][k] = 0.f;
 
-    // weight operand: FP4 one 16-byte piece (hi unused), FP8 the two halves
-    v4u bo[NT], bo_hi[NT], ao[MT];
+    // weight operand: FP4 one 16-byte piece (hi unused), FP8 the two halves;
+    // activation operand likewise (ao_hi for A8 only)
+    v4u bo[NT], bo_hi[NT], ao[MT], ao_hi[MT];
     int bso[NT], aso[MT];
     auto read_ops = [&](int c, int h) {
       const uint8_t* st = smem + (c % S) * STAGE_BYTES;
@@ -829,17 +845,31 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        ao[i] = *reinterpret_cast<const v4u*>(st + a_lds + i * 2048 + h * 512);
-        aso[i] = st[as_lds + i * 128 + 2 * h];
+        if (A8) {
+          ao[i] = *reinterpret_cast<const v4u*>(st + a_lds + i * 4096 + h * 512);
+          ao_hi[i] = *reinterpret_cast<const v4u*>(st + a_lds + i * 4096 + h * 512 + 256);
+          aso[i] = 127;
+        } else {
+          ao[i] = *reinterpret_cast<const v4u*>(st + a_lds + i * 2048 + h * 512);
+          aso[i] = st[as_lds + i * 128 + 2 * h];
+        }
       }
     };
     auto mma = [&]() {
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const v8i af = v8i{(int)ao[i][0], (int)ao[i][1], (int)ao[i][2], (int)ao[i][3], 0, 0, 0, 0};
+        const v8i af = A8 ? v8i{(int)ao[i][0], (int)ao[i][1], (int)ao[i][2], (int)ao[i][3],
+                                (int)ao_hi[i][0], (int)ao_hi[i][1], (int)ao_hi[i][2], (int)ao_hi[i][3]}
+                          : v8i{(int)ao[i][0], (int)ao[i][1], (int)ao[i][2], (int)ao[i][3], 0, 0, 0, 0};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          if (W8) {
+          if (A8) {
+            // A and B format 0 (E4M3), unit block scales
+            const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3],
+                               (int)bo_hi[nt][0], (int)bo_hi[nt][1], (int)bo_hi[nt][2], (int)bo_hi[nt][3]};
+            acc[i][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af, bf, acc[i][nt], 0, 0, 0,
+                                                                        127, 0, 127);
+          } else if (W8) {
             // A format 4 (E2M1), B format 0 (E4M3)
             const v8i bf = v8i{(int)bo[nt][0], (int)bo[nt][1], (int)bo[nt][2], (int)bo[nt][3],
                                (int)bo_hi[nt][0], (int)bo_hi[nt][1], (int)bo_hi[nt][2], (int)bo_hi[nt][3]};
@@ -871,10 +901,15 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
       for (int h = 0; h < 2; ++h) {
         if (h == 0) wait_chunks<D, S - 2>(min(S - 2, nkc - 1 - c));
         wait_lgkm0();
-        if constexpr (W8)
+        if constexpr (A8)
+          asm volatile("s_barrier"
+                       : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[MT - 1][0]), "+v"(acc[MT - 1][1])
+                       :
+                       : "memory");
+        else if constexpr (W8)
           asm volatile("s_barrier"
                        : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
-                         "+v"(acc[2][0]), "+v"(acc[2][1])
+                         "+v"(acc[MT - 1][0]), "+v"(acc[MT - 1][1])
                        :
                        : "memory");
         else
@@ -888,11 +923,17 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
         read_ops(c, h);
         if (h == 1 && grp == 1 && c + 1 < nkc) wait_chunks<D, S - 2>(min(S - 2, nkc - 2 - c));
         wait_lgkm0();
-        if constexpr (W8)
+        if constexpr (A8)
           asm volatile("s_barrier"
                        : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo_hi[0]), "+v"(bo_hi[1]),
-                         "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]),
-                         "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[2])
+                         "+v"(ao[0]), "+v"(ao[MT - 1]), "+v"(ao_hi[0]), "+v"(ao_hi[MT - 1])
+                       :
+                       : "memory");
+        else if constexpr (W8)
+          asm volatile("s_barrier"
+                       : "+v"(bo[0]), "+v"(bo[1]), "+v"(bo_hi[0]), "+v"(bo_hi[1]),
+                         "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[MT - 1]),
+                         "+v"(aso[0]), "+v"(aso[1]), "+v"(aso[MT - 1])
                        :
                        : "memory");
         else
@@ -926,6 +967,18 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
 #pragma unroll
           for (int k = 0; k < 16; ++k) acc[i][nt][k] *= cs;
       }
+    }
+    if constexpr (A8) {
+      // per-row activation scales (the row a sorted row reads)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int r = wrow0 + kb * 4 + i * 32 + (k >> 2) * 8 + (k & 3);
+          const float sa = (r < row_end) ? p.a_row_scale[src_row(r)] : 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[i][nt][k] *= sa;
+        }
     }
     if (p.out_f32) {
       // fp32 copy requested: element-wise stores of both outputs
@@ -1017,14 +1070,14 @@ __global__ __launch_bounds__(512, 1) void mx_dma_wide_gemm_kernel(GemmParams p) 
   }
 }
 
-template <int STAGE, bool W8>
+template <int STAGE, bool W8, bool A8 = false>
 static void launch_mx_wide(const GemmParams& p, int max_tiles, hipStream_t s) {
   const int out_per_wg = ((STAGE == 1) ? 256 : 512) / (W8 ? 2 : 1);
   const int n_out = (STAGE == 1) ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / out_per_wg);
   const int cap = grid_cap() / 8;        // one workgroup (eight waves) per CU
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((mx_dma_wide_gemm_kernel<STAGE, W8>), dim3(grid), dim3(512), 0, s, p);
+  hipLaunchKernelGGL((mx_dma_wide_gemm_kernel<STAGE, W8, A8>), dim3(grid), dim3(512), 0, s, p);
 }
 
 template <int STAGE, int WM>
@@ -1088,6 +1141,11 @@ void launch_mx_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s
 void launch_mx_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
   if (stage == 1) launch_mx_wide<1, true>(p, max_tiles, s);
   else launch_mx_wide<2, true>(p, max_tiles, s);
+}
+
+void launch_fp8_fp8_wide_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
+  if (stage == 1) launch_mx_wide<1, true, true>(p, max_tiles, s);
+  else launch_mx_wide<2, true, true>(p, max_tiles, s);
 }
 
 }  // namespace fp4moe

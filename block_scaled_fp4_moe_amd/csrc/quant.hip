@@ -1,4 +1,5 @@
-// Dynamic activation quantization: mxfp4_quant_1x32 and nvfp4_qdq.
+// Dynamic activation quantization: mxfp4_quant_1x32, nvfp4_qdq and
+// fp8_quant_per_token.
 //
 // mxfp4_quant_1x32 -- [ATOM] "Stage B: Dynamic Activation Quantization":
 // bf16 activations become E2M1 payloads plus one E8M0 scale per 32 values.
@@ -53,6 +54,68 @@ __device__ __forceinline__ float e4m3_rne_sat(float v, uint32_t* code) {
     *code = (uint32_t)(r * 512.f);            // subnormal: r = m * 2^-9
   }
   return r;
+}
+
+// ---- fp8_quant_per_token ------------------------------------------------
+//
+// [GAUDI] "Exact MXFP4 to FP8 per-channel conversion": the FP8 experts run
+// with dynamic per-token FP8 activations.  Per row: s = amax / 448 (1 for a
+// zero row) and code = E4M3(x / s), both IEEE float32 steps, the E4M3
+// rounding to nearest even and saturating (e4m3_rne_sat).  One wavefront per
+// row; lane l owns the 16-byte pieces l, l+64, ... of the row, held in
+// registers between the maximum and the encode.  Output chunk-major: the 128
+// codes of K chunk c of row r at (c * out_rows + r) * 128, so the GEMM copies
+// a tile's chunk as 16-byte pieces of whole rows.
+constexpr int kFp8MaxSteps = 16;   // K <= 64 lanes * 16 steps * 8 values = 8192
+
+// STEPS: 16-byte pieces per lane held in registers, the smallest of 4 / 8 / 16
+// that covers the row (fewer registers, more waves in flight for short rows).
+template <int STEPS>
+__global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restrict__ x, int M,
+                                                        int K, int64_t ldx,
+                                                        const int32_t* __restrict__ row_count,
+                                                        int out_rows, uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rows = row_count ? min(M, *row_count) : M;
+  if (r >= rows) return;
+  const int pieces = K / 8;
+  uint4 v[STEPS];
+  float amax = 0.f;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int j = lane + 64 * st;
+    v[st] = make_uint4(0, 0, 0, 0);
+    if (j < pieces) v[st] = *reinterpret_cast<const uint4*>(x + r * ldx + j * 8);
+    const uint32_t w[4] = {v[st].x, v[st].y, v[st].z, v[st].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      amax = fmaxf(amax, fmaxf(fabsf(bf16_to_f32(w[i] & 0xffffu)), fabsf(bf16_to_f32(w[i] >> 16))));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  const float sc = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  if (lane == 0) scales[r] = sc;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int j = lane + 64 * st;
+    if (j >= pieces) break;
+    const uint32_t w[4] = {v[st].x, v[st].y, v[st].z, v[st].w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t b = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xffffu);
+      const float q = __fdiv_rn(bf16_to_f32(b), sc);
+      uint32_t c;
+      e4m3_rne_sat(fabsf(q), &c);
+      c |= (b & 0x8000u) ? 0x80u : 0u;          // the sign of x (and of q), zero included
+      out[i >> 2] |= c << (8 * (i & 3));
+    }
+    const int64_t chunk = j >> 4;
+    *reinterpret_cast<uint2*>(codes + (chunk * out_rows + r) * 128 + (j & 15) * 8) =
+        make_uint2(out[0], out[1]);
+  }
 }
 
 // ---- mxfp4_quant_1x32 ---------------------------------------------------
@@ -280,6 +343,33 @@ extern "C" int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t
                      as_stream(stream), x, M, K, ldx, nullptr, row_map, map_k, out_rows,
                      row_count, codes, scales);
   return check_launch("mxfp4_quant_1x32_chunked");
+}
+
+extern "C" int fp8_quant_per_token(const uint16_t* x, int M, int K, int64_t ldx,
+                                   const int32_t* row_count, int out_rows, uint8_t* codes,
+                                   float* scales, void* stream) {
+  FP4MOE_REQUIRE(M >= 0 && K > 0 && K % 128 == 0 && K <= 64 * kFp8MaxSteps * 8,
+                 "fp8_quant_per_token: M=%d K=%d (K a multiple of 128, at most %d)", M, K,
+                 64 * kFp8MaxSteps * 8);
+  FP4MOE_REQUIRE(ldx >= K && ldx % 8 == 0, "fp8_quant_per_token: ldx=%lld", (long long)ldx);
+  FP4MOE_REQUIRE(out_rows >= M, "fp8_quant_per_token: out_rows=%d < M=%d", out_rows, M);
+  if (M == 0) return FP4MOE_OK;
+  FP4MOE_REQUIRE(x && codes && scales, "fp8_quant_per_token: null pointer");
+  FP4MOE_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)codes & 15) == 0,
+                 "fp8_quant_per_token: x and codes must be 16-byte aligned");
+  FP4MOE_CHECK_DEVICE();
+  const dim3 grid((unsigned)((M + 3) / 4));
+  const int steps = (K / 8 + 63) / 64;
+  if (steps <= 4)
+    hipLaunchKernelGGL(fp8_quant_kernel<4>, grid, dim3(256), 0, as_stream(stream), x, M, K, ldx,
+                       row_count, out_rows, codes, scales);
+  else if (steps <= 8)
+    hipLaunchKernelGGL(fp8_quant_kernel<8>, grid, dim3(256), 0, as_stream(stream), x, M, K, ldx,
+                       row_count, out_rows, codes, scales);
+  else
+    hipLaunchKernelGGL(fp8_quant_kernel<kFp8MaxSteps>, grid, dim3(256), 0, as_stream(stream), x,
+                       M, K, ldx, row_count, out_rows, codes, scales);
+  return check_launch("fp8_quant_per_token");
 }
 
 extern "C" size_t nvfp4_qdq_workspace(void) { return 256; }

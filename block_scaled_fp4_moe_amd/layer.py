@@ -16,10 +16,11 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (A_BF16, A_F16, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4, LAYOUT_FRAGMENT,
-               LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle, moe_combine,
-               moe_decode_fused, moe_permute, moe_permute_max_tiles, moe_route,
-               moe_route_permute, mxfp4_quant_1x32, mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
+from . import (A_BF16, A_F16, A_FP8, A_LAYOUT_CHUNKED, A_LAYOUT_ROWMAJOR, A_MXFP4,
+               LAYOUT_FRAGMENT, LAYOUT_ROWMAJOR, WFMT, fp4_grouped_gemm, fp4_weight_preshuffle,
+               fp8_quant_per_token, moe_combine, moe_decode_fused, moe_permute,
+               moe_permute_max_tiles, moe_route, moe_route_permute, mxfp4_quant_1x32,
+               mxfp4_quant_1x32_chunked, nvfp4_qdq, load)
 
 
 # moe_route_permute (one launch, one workgroup) takes T * (topk + n_shared) up
@@ -41,7 +42,7 @@ class LayerConfig:
     n_group: int
     topk_group: int
     topk: int
-    afmt: str              # bf16 | mx | nvfp4
+    afmt: str              # bf16 | mx | nvfp4 | fp8 (per-token FP8, with FP8 weights)
     wfmt: str              # mx | nvfp4 | fp8
     block_m: int = 16
     renormalize: bool = True
@@ -88,6 +89,10 @@ class MoELayer:
         # NVFP4 with 64-row tiles: activations in the f16 operand form of
         # nvfp4_qdq (E2M1 x E4M3 weights decode to f16 with one packed multiply
         # per pair, and the 32x32 f16 MFMA runs at twice the 16x16 bf16 rate)
+        # W8A8: per-token FP8 activations (chunk-major) x FP8 weights, 128-row tiles
+        self.a8 = cfg.afmt == "fp8"
+        if self.a8 and not (cfg.wfmt == "fp8" and cfg.block_m == 128 and cfg.fragment_layout):
+            raise ValueError("FP8 activations run with FP8 fragment-major weights and block_m 128")
         n13, n2 = cfg.I, cfg.H
         self.f16a = (cfg.afmt == "nvfp4" and cfg.wfmt == "nvfp4" and cfg.block_m == 64 and
                      cfg.fragment_layout and n13 % 128 == 0 and n2 % 256 == 0)
@@ -139,6 +144,11 @@ class MoELayer:
             b["xs"] = torch.empty((T, c.H // 32), dtype=torch.uint8, device=dev)
             b["hq"] = torch.empty((P, c.I // 2), dtype=torch.uint8, device=dev)
             b["hs"] = torch.empty((P, c.I // 32), dtype=torch.uint8, device=dev)
+        elif c.afmt == "fp8":
+            b["xq"] = torch.empty((c.H // 128, T, 128), dtype=torch.uint8, device=dev)
+            b["xs"] = torch.empty(T, dtype=torch.float32, device=dev)
+            b["hq"] = torch.empty((c.I // 128, P, 128), dtype=torch.uint8, device=dev)
+            b["hs"] = torch.empty(P, dtype=torch.float32, device=dev)
         elif c.afmt == "nvfp4":
             dt = torch.float16 if self.f16a else torch.bfloat16
             b["xq"] = torch.empty((T, c.H), dtype=dt, device=dev)
@@ -199,6 +209,10 @@ class MoELayer:
         elif c.afmt == "mx":
             mxfp4_quant_1x32(x, codes=b["xq"], scales=b["xs"], stream=stream)
             a1, a1s, af = b["xq"], b["xs"], A_MXFP4
+        elif c.afmt == "fp8":
+            fp8_quant_per_token(x, codes=b["xq"], scales=b["xs"], stream=stream)
+            a1, a1s, af = b["xq"], None, A_FP8
+            a_layout = A_LAYOUT_CHUNKED
         elif c.afmt == "nvfp4" and self.f16a:
             nvfp4_qdq(x, y_f16=b["xq"], y_f16_scale=b["xs"], no_y=True,
                       workspace=self.nvfp4_ws, stream=stream)
@@ -216,6 +230,8 @@ class MoELayer:
         fused_q = self.chunked and c.block_m == 192
         qkw = dict(out_q=b["hq"], out_q_scale=b["hs"], no_out=not keep) if fused_q else {}
         f16kw = dict(a_f16_scale=b["xs"]) if self.f16a else {}
+        if self.a8:
+            f16kw = dict(a_row_scale=b["xs"])
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
                          perm, c.block_m, a_scale=a1s, w_tensor_scale=ts13, w_channel_scale=cs13,
                          out=b["h"] if (keep or not fused_q) else None, w_layout=self.layout,
@@ -232,6 +248,10 @@ class MoELayer:
             mxfp4_quant_1x32(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
                              stream=stream)
             a2, a2s = b["hq"], b["hs"]
+        elif c.afmt == "fp8":
+            fp8_quant_per_token(b["h"], row_count=n_rows, codes=b["hq"], scales=b["hs"],
+                                stream=stream)
+            a2, a2s = b["hq"], None
         elif c.afmt == "nvfp4" and self.f16a:
             nvfp4_qdq(b["h"], row_count=n_rows, y_f16=b["hq"], y_f16_scale=b["hs"], no_y=True,
                       workspace=self.nvfp4_ws, stream=stream)
@@ -246,6 +266,8 @@ class MoELayer:
         cs2 = w["w2_scale"] if c.wfmt == "fp8" else None
         tick("stage2")
         f16kw = dict(a_f16_scale=b["hs"]) if self.f16a else {}
+        if self.a8:
+            f16kw = dict(a_row_scale=b["hs"])
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,
                          c.block_m, a_scale=a2s, w_tensor_scale=ts2, w_channel_scale=cs2,
                          out=b["y"], w_layout=self.layout, a_layout=a_layout, stream=stream,

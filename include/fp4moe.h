@@ -61,8 +61,10 @@ enum {
 enum {
   FP4MOE_A_BF16 = 0,   /* bf16 [rows, K]: weights are decoded to bf16 inside the GEMM tile  */
   FP4MOE_A_MXFP4 = 1,  /* E2M1 codes [rows, K/2] + E8M0 [rows, K/32]: gfx950 scaled MFMA    */
-  FP4MOE_A_F16 = 2     /* f16 [rows, K] times the power of two *a_f16_scale: the f16 form
+  FP4MOE_A_F16 = 2,    /* f16 [rows, K] times the power of two *a_f16_scale: the f16 form
                           that nvfp4_qdq writes; NVFP4 weights decoded to f16 in the tile  */
+  FP4MOE_A_FP8 = 3     /* E4M3 codes, chunk-major [K/128, a_rows, 128], times one float
+                          per row (a_row_scale): fp8_quant_per_token's output (W8A8)       */
 };
 
 /* Layouts of MXFP4 activations (see mxfp4_quant_1x32_chunked). */
@@ -199,6 +201,22 @@ int mxfp4_quant_1x32_chunked(const uint16_t* x, int M, int K, int64_t ldx, const
                              uint8_t* scales, void* stream);
 
 /*
+ * fp8_quant_per_token -- dynamic per-token FP8 quantization of bf16 rows (the
+ * W8A8 activations).  [GAUDI] "Exact MXFP4 to FP8 per-channel conversion":
+ * the FP8 experts are served with dynamic per-token FP8 activations.
+ * Per row r, IEEE float32 steps: s_r = amax_r / 448 (1 for an all-zero row);
+ * code = E4M3FN of x / s_r, round to nearest even, saturating at +-448, the
+ * sign of x kept (also for zero).
+ * x bf16 [M, K] with row stride ldx (elements; ldx % 8 == 0); rows at or past
+ * *row_count (device, NULL = M) are not written.  Output: codes chunk-major
+ * [K/128, out_rows, 128] (row r's codes of K chunk c at (c*out_rows + r)*128)
+ * and scales float [out_rows]; out_rows >= M.  K % 128 == 0, K <= 8192;
+ * x and codes 16-byte aligned.
+ */
+int fp8_quant_per_token(const uint16_t* x, int M, int K, int64_t ldx, const int32_t* row_count,
+                        int out_rows, uint8_t* codes, float* scales, void* stream);
+
+/*
  * nvfp4_qdq -- NVFP4 quantize-dequantize round trip of bf16 activations.
  * [NVFP4] "Weight Dequantization and Activation QDQ".  IEEE float32 steps:
  *   s_t = tensor_scale_in ? *tensor_scale_in : amax(|x|)/2688 (1 if amax = 0)
@@ -243,12 +261,19 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  *     scaled MFMA, FP4 x FP4, both E8M0 scales as MFMA scale operands;
  *   (FP8, MXFP4) with block_m 192: the gfx950 scaled MFMA in its FP4 x FP8
  *     form (E4M3 weights, E2M1 activations, unit block scales), the per-row
- *     channel scale applied in the epilogue.
+ *     channel scale applied in the epilogue;
+ *   (FP8, FP8) with block_m 128: W8A8 ([GAUDI] "Exact MXFP4 to FP8 per-channel
+ *     conversion": per-channel FP8 weights, dynamic per-token FP8
+ *     activations) on the gfx950 scaled MFMA with both operands E4M3 and unit
+ *     block scales; a_row_scale[row] and the channel scale multiply the
+ *     accumulators in the epilogue.  Fragment-major weights, a_layout
+ *     FP4MOE_A_LAYOUT_CHUNKED (fp8_quant_per_token's layout; a row gather, if
+ *     given, picks the activation row and its scale), no out_q.
  * K % 128 == 0, N % 32 == 0 (stage 1: N % 64 == 0).  The output width (N/2
  * in stage 1, N in stage 2) must be a multiple of: 64 / 128 for (MXFP4,
  * MXFP4) at block_m 32 or 64, 128 / 256 at block_m 128 or 256, 256 / 512 at
- * block_m 192; 128 / 256 for (FP8, MXFP4) at block_m 192 and for (NVFP4,
- * F16).  block_m 192 needs fragment-major weights.  With fragment-major
+ * block_m 192; 128 / 256 for (FP8, MXFP4) at block_m 192, for (FP8, FP8) and
+ * for (NVFP4, F16).  block_m 192 needs fragment-major weights.  With fragment-major
  * weights, block_m >= 128 and row-major A, the scaled-MFMA tiles need
  * max_rows * lda / 2 < 2^32 and gathered rows < max_rows.
  * a_layout FP4MOE_A_LAYOUT_CHUNKED (codes and scales of a_rows rows in the
@@ -301,6 +326,7 @@ typedef struct {
   uint8_t* out_q_scale;    /*   and its E8M0 scales (see below)                     */
   int out_q_rows;          /*   rows per K chunk slab of out_q / out_q_scale        */
   const float* a_f16_scale;  /* FP4MOE_A_F16: device [1], the power-of-two factor   */
+  const float* a_row_scale;  /* FP4MOE_A_FP8: device [a_rows], one scale per row of a */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = fm.load()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in ["moe_route", "moe_permute", "mxfp4_quant_1x32", "nvfp4_qdq", "fp4_grouped_gemm",
               "moe_combine", "mxfp4_to_fp8_channel", "mxfp4_quant_1x32_chunked",
               "moe_route_permute", "mxfp4_linear"]:
@@ -110,7 +110,8 @@ def test_gemm_rejects_unsupported_combinations():
                            None, None, None, None, None, None, a["lda"], None, None, None, None,
                            None, a["ldo"], a.get("out_f32"), a.get("w_layout", 0),
                            a.get("a_layout", 0), a.get("a_rows", 0), a.get("out_q"),
-                           a.get("out_q_scale"), a.get("out_q_rows", 0), a.get("a_f16_scale"))
+                           a.get("out_q_scale"), a.get("out_q_rows", 0), a.get("a_f16_scale"),
+                           a.get("a_row_scale"))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -160,6 +161,19 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**wide, **q, stage=2)[0] == 1
     assert run(**{**wide, "block_m": 256, "ldo": 256}, **q)[0] == 1
     assert run(**wide, **{**q, "out_q_rows": 4})[0] == 1       # < max_rows
+    # W8A8: FP8 weights x FP8 activations, block_m 128, fragment weights,
+    # chunk-major activations, a row-scale pointer, output width a multiple of
+    # 128 (stage 1) / 256 (stage 2), no quantized stage-1 output
+    w8a8 = dict(wfmt=2, afmt=3, block_m=128, w_layout=1, a_layout=1, a_rows=8, N=256, ldo=256)
+    assert run(**w8a8, max_tiles=0)[0] == 0
+    assert run(**w8a8, stage=2, max_tiles=0)[0] == 0
+    assert run(**{**w8a8, "wfmt": 0}, max_tiles=0)[0] == 1      # MXFP4 weights
+    assert run(**{**w8a8, "block_m": 192}, max_tiles=0)[0] == 1
+    assert run(**{**w8a8, "w_layout": 0}, max_tiles=0)[0] == 1
+    assert run(**{**w8a8, "a_layout": 0}, max_tiles=0)[0] == 1
+    assert run(**{**w8a8, "N": 320}, max_tiles=0)[0] == 1       # output width 160
+    assert run(**w8a8, **q)[0] == 1
+    assert run(**w8a8)[0] == 1                                   # null pointers with work
     assert run(**wide, **q, out_f32=256)[0] == 1
     # f16 activations (the NVFP4 operand form): NVFP4 fragment weights, block_m 64
     f16 = dict(wfmt=1, afmt=2, block_m=64, w_layout=1, N=512, ldo=256, max_tiles=0)
@@ -260,3 +274,15 @@ def test_decode_fused_rejects_bad_arguments(bad):
     # T = 0 with valid sizes is accepted and does nothing
     a = _decode_args(T=0, max_tiles=0, workspace_bytes=ws)
     assert _status(lambda lib: lib.moe_decode_fused(ctypes.byref(a), None))[0] == 0
+
+
+def test_fp8_quant_rejects_bad_arguments():
+    """Shape and layout checks of fp8_quant_per_token before any device work."""
+    fake = ctypes.c_void_p(4096)
+    for M, K, ldx, out_rows in [(4, 96, 96, 4), (4, 8320, 8320, 4), (4, 256, 200, 4),
+                                (4, 256, 256, 3), (-1, 256, 256, 4)]:
+        st, msg = _status(lambda lib: lib.fp8_quant_per_token(fake, M, K, ldx, None, out_rows,
+                                                              fake, fake, None))
+        assert st == 1 and "fp8_quant_per_token" in msg, (M, K, ldx, out_rows, msg)
+    assert _status(lambda lib: lib.fp8_quant_per_token(None, 0, 256, 256, None, 0, None, None,
+                                                       None))[0] == 0

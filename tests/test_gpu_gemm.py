@@ -95,6 +95,17 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
             qs = qs.copy()
             qs[n_rows:] = 255
         a_kw = dict(a=dev(qc), a_scale=dev(qs), afmt=gpu_lib.A_MXFP4)
+    elif afmt == "fp8":
+        # per-token FP8 from the oracle's quantizer, chunk-major; rows past the
+        # valid count poisoned (NaN codes, NaN scales) for stage 2
+        codes, sc = OQ.fp8_quant_per_token(xb)
+        a_vals = F.e4m3_decode(codes) * sc.astype(np.float64)[:, None]
+        if poison:
+            codes, sc = codes.copy(), sc.copy()
+            codes[n_rows:] = 0x7F
+            sc[n_rows:] = np.nan
+        cm = np.ascontiguousarray(codes.reshape(rows_in, K // 128, 128).transpose(1, 0, 2))
+        a_kw = dict(a=dev(cm), a_row_scale=dev(sc), afmt=gpu_lib.A_FP8)
     elif afmt == "f16":
         # NVFP4 activations in the f16 operand form, made on the host from the
         # oracle's QDQ: y * 2^-p is exact in f16
@@ -122,7 +133,7 @@ def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=F
     else:
         a_sorted = a_vals[:n_rows]
         gather = {}
-    if a_layout == 1:
+    if a_layout == 1 and afmt == "mx":
         # chunk-major activations, already in expert order (stage 1: gathered
         # here, on the host), rows past the valid count poisoned
         rows = T * k
@@ -456,3 +467,31 @@ def test_mxfp4_linear_full_size_sampled(gpu_lib):
     gpu_lib.mxfp4_linear(codes, scales, fc[0], fs[0], a_layout=1, M=M, out=out2)
     assert_bf16_close(bits_of(out2)[rows], ref, "full-size mxfp4_linear, bf16-only epilogue")
     assert not torch.isnan(out2).any().item(), "bf16-only epilogue left rows unwritten"
+
+
+W8A8_CASES = [
+    # stage, T, topk, E, ns, H, I, seed, skew: 128-row tiles, several per expert
+    # with ragged tails, a shared expert, the full layer width
+    (1, 300, 4, 8, 1, 512, 256, 60, False),
+    (2, 300, 4, 8, 1, 512, 256, 61, False),
+    (1, 600, 2, 5, 1, 512, 256, 62, True),
+    (2, 600, 2, 5, 1, 1024, 256, 63, True),
+    (1, 40, 8, 16, 1, 7168, 2048, 64, False),
+    (2, 40, 8, 16, 1, 7168, 2048, 65, False),
+]
+
+
+@pytest.mark.parametrize("case", W8A8_CASES)
+def test_w8a8_gemm_parity(gpu_lib, case):
+    """FP8 weights (fragment-major, per-channel scales) x per-token FP8
+    activations (chunk-major) on the scaled MFMA, 128-row tiles: float32 and
+    bf16 outputs against the oracle on the same FP8 values."""
+    stage, T, topk, E, ns, H, I, seed, skew = case
+    run_stage(gpu_lib, stage, "fp8", "fp8", T, topk, E, ns, H, I, 128, seed, skew=skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=1)
+
+
+def test_w8a8_gemm_bf16_only(gpu_lib):
+    """The bf16-only epilogue (the one the layer runs) of the W8A8 tiles."""
+    run_stage(gpu_lib, 2, "fp8", "fp8", 300, 4, 8, 1, 512, 256, 128, 66,
+              layout=gpu_lib.LAYOUT_FRAGMENT, a_layout=1, with_f32=False)

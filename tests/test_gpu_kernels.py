@@ -437,3 +437,57 @@ def test_combine_parity(gpu_lib, T, topk, ns, H):
     ref, _ = OG.moe_combine(F.bf16_decode(y), pos, w.astype(np.float64), T, topk, ns)
     assert_bf16_close(bits_of(out), ref, "combine")
     assert_float_close(host(out_f32), ref, "combine f32", rel_l2=1e-6, max_abs_rms=1e-5)
+
+
+# ------------------------------------------------------------------ FP8 per token
+
+def _fp8_rows(host_codes):
+    """chunk-major [K/128, rows, 128] -> row-major [rows, K]."""
+    c = np.asarray(host_codes)
+    return np.ascontiguousarray(c.transpose(1, 0, 2)).reshape(c.shape[1], -1)
+
+
+@pytest.mark.parametrize("M,K", [(33, 128), (7, 7168), (300, 2048), (5, 8192)])
+def test_fp8_quant_per_token_parity(gpu_lib, M, K):
+    """Codes (chunk-major) and per-row scales bit-exact against the oracle, rows
+    of magnitudes 2^-12 .. 2^12, a zero row and a row of negative zeros."""
+    g = np.random.default_rng(M * K)
+    x = g.standard_normal((M, K)).astype(np.float32) * np.exp2(g.uniform(-12, 12, (M, 1))).astype(np.float32)
+    x[0] = 0.0
+    if M > 1:
+        x[1] = -0.0
+    xb = synth.bf16_from_f32(x)
+    codes, scales = gpu_lib.fp8_quant_per_token(bf16_dev(xb))
+    rc, rs = OQ.fp8_quant_per_token(xb)
+    assert_equal(_fp8_rows(host(codes)), rc, "fp8 codes")
+    assert_equal(host(scales), rs, "fp8 row scales")
+
+
+def test_fp8_quant_every_finite_bf16(gpu_lib):
+    """Every finite bf16 pattern (non-finite ones replaced by zero), 32 rows of
+    2048, through the GPU quantizer and the oracle: bit-exact codes and scales
+    (the division and the E4M3 rounding, ties and subnormals included)."""
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = (pats & 0x7F80) != 0x7F80
+    xb = np.where(finite, pats, 0).astype(np.uint16).reshape(32, 2048)
+    codes, scales = gpu_lib.fp8_quant_per_token(bf16_dev(xb))
+    rc, rs = OQ.fp8_quant_per_token(xb)
+    assert_equal(_fp8_rows(host(codes)), rc, "fp8 codes, every finite bf16")
+    assert_equal(host(scales), rs, "fp8 row scales, every finite bf16")
+
+
+def test_fp8_quant_row_count_and_slab(gpu_lib):
+    """Rows at or past the device row count are not written; the output slab
+    may be taller than M."""
+    M, K, out_rows = 40, 256, 48
+    g = np.random.default_rng(5)
+    xb = synth.bf16_from_f32(g.standard_normal((M, K)).astype(np.float32))
+    codes = torch.full((K // 128, out_rows, 128), 0xEE, dtype=torch.uint8, device="cuda")
+    scales = torch.full((out_rows,), -1.0, dtype=torch.float32, device="cuda")
+    gpu_lib.fp8_quant_per_token(bf16_dev(xb), row_count=dev(np.array([29], np.int32)),
+                                out_rows=out_rows, codes=codes, scales=scales)
+    rc, rs = OQ.fp8_quant_per_token(xb[:29])
+    hc, hs = _fp8_rows(host(codes)), host(scales)
+    assert_equal(hc[:29], rc, "codes of the counted rows")
+    assert_equal(hs[:29], rs, "scales of the counted rows")
+    assert np.all(hc[29:] == 0xEE) and np.all(hs[29:] == -1.0), "rows past the count"

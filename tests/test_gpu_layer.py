@@ -299,10 +299,11 @@ def sample_tokens(perm, k, T, E, n_shared, block_m, rng, n=32):
 END_TO_END_REL_L2 = 5e-3
 
 
-def _full_size_layer(gpu_lib, wname, wfmt, seed):
+def _full_size_layer(gpu_lib, wname, wfmt, seed, afmt="mx"):
     """The MXFP4-activation layer at a benchmarked size and launch configuration
-    (192-row tiles, h quantized in the stage-1 epilogue; the bf16 copy of h is
-    also kept for the check).  Every token: routing ids and the permutation
+    (192-row tiles, h quantized in the stage-1 epilogue; W8A8: 128-row tiles,
+    h quantized per row by fp8_quant_per_token; the bf16 copy of h is also
+    kept for the check).  Every token: routing ids and the permutation
     bit-exact.  At least 32 sampled tokens (sample_tokens), stage by stage on
     the GPU's own upstream outputs (a token's rows depend only on its own row,
     its routing and the weights):
@@ -327,8 +328,9 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
     bias = synth.router_bias(w)
     xb = synth.activations(w, T, 0)
     rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    perm = OP.moe_permute(rid, w.E, w.n_shared, 192)
-    sub = sample_tokens(perm, k, T, w.E, w.n_shared, 192, np.random.default_rng(seed))
+    bm = 128 if afmt == "fp8" else 192
+    perm = OP.moe_permute(rid, w.E, w.n_shared, bm)
+    sub = sample_tokens(perm, k, T, w.E, w.n_shared, bm, np.random.default_rng(seed))
     need = set(rid[sub].reshape(-1).tolist()) | set(range(w.E, Et))
     np_w = dict(w13={}, w13_scale={}, w2={}, w2_scale={})
     if wfmt == "mx":
@@ -362,8 +364,8 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
                 if e in need:
                     np_w[name][e], np_w[name + "_scale"][e] = c, sc
     cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
-                              topk_group=w.topk_group, topk=w.topk, afmt="mx", wfmt=wfmt,
-                              block_m=192)
+                              topk_group=w.topk_group, topk=w.topk, afmt=afmt, wfmt=wfmt,
+                              block_m=bm)
     layer = gpu_lib.MoELayer(cfg, dev_w)
     del dev_w
     b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
@@ -407,12 +409,22 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
     h_cols = (hb[:, None] * 32 + np.arange(32)).reshape(-1)
     y_cols = np.unique(np.concatenate([np.arange(64), np.arange(H - 64, H),
                                        g.choice(H, 384, replace=False)]))
-    # activation codes of the sampled tokens (written to each of their rows)
-    xc, xs = chunked_rows(b["xq"], b["xs"])
-    qc, qs = OQ.mxfp4_quant_1x32(xb[sub])
-    assert_equal(xc, np.repeat(qc, k, axis=0), "activation codes (sampled rows)")
-    assert_equal(xs, np.repeat(qs, k, axis=0), "activation scales (sampled rows)")
-    a1 = np.repeat(F.mxfp4_dequant(qc, qs), k, axis=0)
+    if afmt == "fp8":
+        # per-token FP8 codes of the sampled tokens (one row per token)
+        sub_d = torch.from_numpy(sub.astype(np.int64)).cuda()
+        xc = host(b["xq"].index_select(1, sub_d).permute(1, 0, 2).reshape(len(sub), -1))
+        xs = host(b["xs"].index_select(0, sub_d))
+        qc, qs = OQ.fp8_quant_per_token(xb[sub])
+        assert_equal(xc, qc, "activation codes (sampled tokens)")
+        assert_equal(xs, qs, "activation scales (sampled tokens)")
+        a1 = np.repeat(F.e4m3_decode(qc) * qs.astype(np.float64)[:, None], k, axis=0)
+    else:
+        # activation codes of the sampled tokens (written to each of their rows)
+        xc, xs = chunked_rows(b["xq"], b["xs"])
+        qc, qs = OQ.mxfp4_quant_1x32(xb[sub])
+        assert_equal(xc, np.repeat(qc, k, axis=0), "activation codes (sampled rows)")
+        assert_equal(xs, np.repeat(qs, k, axis=0), "activation scales (sampled rows)")
+        a1 = np.repeat(F.mxfp4_dequant(qc, qs), k, axis=0)
     print(f"[{wname}/{wfmt}] {len(sub)} tokens, {len(rows)} rows, "
           f"{len(np.unique(row_e))} experts: activation codes ok", flush=True)
     # stage 1 on the checked h columns (gate rows h_cols, up rows I + h_cols)
@@ -421,12 +433,21 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
     h_ref = per_expert("w13", wr13, a1, lambda a, wt: OG.stage1_expert(a, wt))
     assert_bf16_close(h_gpu[:, h_cols], h_ref, "h (sampled rows, checked columns)")
     print(f"[{wname}/{wfmt}] stage 1 ok", flush=True)
-    # the epilogue's MXFP4 codes of h, full rows
-    hc, hs = chunked_rows(b["hq"], b["hs"])
-    rc, rs = OQ.mxfp4_quant_1x32(h_gpu)
-    assert_equal(hc, rc, "h codes from the stage-1 epilogue (sampled rows)")
-    assert_equal(hs, rs, "h scales from the stage-1 epilogue (sampled rows)")
-    a2 = F.mxfp4_dequant(hc, hs)
+    if afmt == "fp8":
+        # the per-row FP8 codes of h (fp8_quant_per_token on the GPU's h), full rows
+        hc = host(b["hq"].index_select(1, rows_d).permute(1, 0, 2).reshape(len(rows), -1))
+        hs = host(b["hs"].index_select(0, rows_d))
+        rc, rs = OQ.fp8_quant_per_token(h_gpu)
+        assert_equal(hc, rc, "h FP8 codes (sampled rows)")
+        assert_equal(hs, rs, "h FP8 row scales (sampled rows)")
+        a2 = F.e4m3_decode(hc) * hs.astype(np.float64)[:, None]
+    else:
+        # the epilogue's MXFP4 codes of h, full rows
+        hc, hs = chunked_rows(b["hq"], b["hs"])
+        rc, rs = OQ.mxfp4_quant_1x32(h_gpu)
+        assert_equal(hc, rc, "h codes from the stage-1 epilogue (sampled rows)")
+        assert_equal(hs, rs, "h scales from the stage-1 epilogue (sampled rows)")
+        a2 = F.mxfp4_dequant(hc, hs)
     # stage 2 on the GPU's h codes, checked y columns
     y_gpu = host(b["y"].index_select(0, rows_d).view(torch.int16)).view(np.uint16)
     y_ref = per_expert("w2", y_cols, a2, lambda a, wt: OG.stage2_expert(a, wt))
@@ -440,8 +461,8 @@ def _full_size_layer(gpu_lib, wname, wfmt, seed):
     # end to end on four of the tokens
     e2e = sub[:: max(1, len(sub) // 4)][:4]
     ref = OL.moe_layer(xb[e2e], logits[e2e], bias, np_w, E=w.E, n_shared=w.n_shared,
-                       n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt="mx",
-                       wfmt=wfmt, block_m=192, topk_ids=rid[e2e], topk_w=rw[e2e])
+                       n_group=w.n_group, topk_group=w.topk_group, topk=w.topk, afmt=afmt,
+                       wfmt=wfmt, block_m=bm, topk_ids=rid[e2e], topk_w=rw[e2e])
     stats = assert_float_close(F.bf16_decode(bits_of(b["out"])[e2e]), F.bf16_round(ref["out"]),
                                "out end to end", rel_l2=END_TO_END_REL_L2, max_abs_rms=1.0)
     print(f"[{wname}/{wfmt}] combine ok; end-to-end rel-L2 {stats['rel_l2']:.2e}", flush=True)
@@ -461,6 +482,13 @@ def test_layer_skewed_prefill_full_size_sampled(gpu_lib):
     M tiles; its first and last tiles are among the sampled rows."""
     counts = _full_size_layer(gpu_lib, "skewed", "mx", 12)
     assert counts[:384].max() > 8 * 192          # the routing really is skewed
+
+
+def test_layer_w8a8_full_size_sampled(gpu_lib):
+    """W8A8 at T=16384 with Zipf(1.1) routing: per-token FP8 activations x E4M3
+    weights with power-of-two channel scales on the 128-row FP8 x FP8
+    scaled-MFMA tiles (see _full_size_layer)."""
+    _full_size_layer(gpu_lib, "skewed", "fp8", 14, afmt="fp8")
 
 
 def test_layer_fp8_full_size_sampled(gpu_lib):
@@ -618,6 +646,17 @@ def test_layer_nvfp4_is_deterministic(gpu_lib):
 @pytest.mark.parametrize("block_m", [32, 64, 192])
 def test_layer_fp8_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "mx", "fp8", block_m)
+
+
+def test_layer_w8a8_full_width(gpu_lib):
+    """W8A8 (per-token FP8 activations, the oracle's exact FP8 conversion of the
+    MXFP4 experts) at full width; several 128-row tiles per expert are covered
+    by test_w8a8_gemm_parity and the full-size test."""
+    run_layer(gpu_lib, synth.WORKLOADS["skewed"], 6, "fp8", "fp8", 128)
+
+
+def test_layer_w8a8_is_deterministic(gpu_lib):
+    _twice(gpu_lib, synth.WORKLOADS["skewed"], 6, "fp8", "fp8", 128)
 
 
 def test_layer_fp8_is_deterministic(gpu_lib):
