@@ -54,7 +54,18 @@ N_ROTATE = 16
 # for a plain 1 GiB copy (FETCH_SIZE reads half the bytes: x1.9999; WRITE_SIZE
 # x1.0).  Reported only while the kernel's sources hash to what they were when
 # the counters were taken; otherwise traffic is null.  Keyed by kernel.
-ROOFLINE_COUNTERS = {}
+ROOFLINE_COUNTERS = {
+    "stage1": dict(
+        tokens=8, fetch_kib=378988.3, write_kib=288.0, fetch_scale=1.9999, write_scale=1.0,
+        sources=("block_scaled_fp4_moe_amd/csrc/gemm_dq.hip",
+                 "block_scaled_fp4_moe_amd/csrc/dq_item.h",
+                 "block_scaled_fp4_moe_amd/csrc/gemm_common.h",
+                 "block_scaled_fp4_moe_amd/csrc/common.h"),
+        sha256=("237f7aabeb9862f75362261cdfd07d2873ad244bcaf1a0bacca908f035546f26",
+                "b093c60db7909994542252865dae0a72a06224d6e2ba49d207411efd98846d82",
+                "d0ae32a13fb9a774a315dbdf9c73817cc42ca9f2669bd57489ece84cb5d84a2d",
+                "3af844087c30bbbc3272119b6ca934e877d90b1159a2b45ad9077007c79fd1c0")),
+}
 
 
 def roofline_traffic(kernel, tokens):
@@ -757,8 +768,8 @@ def main():
             "traffic": traffic,
             "traffic_source": ("stored, not measured by this run: two rocprofv3 --pmc passes "
                                "(FETCH_SIZE, WRITE_SIZE) of this kernel on this workload, "
-                               "profiles/; reported only while the kernel's sources hash as "
-                               "they did then" if traffic is not None else
+                               "profiles/dq_gemm_decode_T8_hbm_counters.md; reported only while "
+                               "the kernel's sources hash as they did then" if traffic is not None else
                                "null: no counter passes of this kernel as it is now"),
             "avg_launch_us": round(s1["ms"] * 1e3, 2),
             "algorithmic_bytes_per_launch": int(s1["bytes"]),
