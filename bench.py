@@ -403,7 +403,7 @@ def run_nvfp4(fm, steps, torch, args):
     dev_w = gpu_nvfp4_weights(w, torch)
     cfg = fm.LayerConfig(H=w.H, I=w.I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                          topk_group=w.topk_group, topk=w.topk, afmt="nvfp4", wfmt="nvfp4",
-                         block_m=64)
+                         block_m=128)
     layer = fm.MoELayer(cfg, dev_w)
     del dev_w
     bias = torch.from_numpy(synth.router_bias(w)).cuda()
@@ -421,8 +421,8 @@ def run_nvfp4(fm, steps, torch, args):
                 experts_per_step=round(r["touched_per_step"], 1),
                 kernels_ms={k: round(v, 4) for k, v in r["per_kernel_ms"].items()},
                 workload=f"NVFP4 emulation MoE layer, T={w.T}, 384 experts top-8, E4M3 per-16 "
-                         "weight scales + fp32 tensor scale decoded to bf16 in-tile, activation "
-                         "QDQ before each GEMM; weights drawn on the GPU")
+                         "weight scales + fp32 tensor scale decoded to f16 in-tile (128-row "
+                         "tiles), activation QDQ before each GEMM; weights drawn on the GPU")
 
 
 def run_fp8(fm, steps, torch, args):

@@ -1,9 +1,15 @@
 // fp4_grouped_gemm entry point: argument checks and family dispatch.  The
-// kernels live in gemm_dq.hip (bf16 MFMA on decoded weights) and gemm_mx.hip
-// (scaled FP4 MFMA); gemm_common.h holds the operand conventions.
+// kernels live in gemm_dq.hip / gemm_dqt.hip (bf16 or f16 MFMA on decoded
+// weights), gemm_nvf16.hip (NVFP4 x f16 in 128-row tiles) and gemm_mx.hip
+// (scaled FP4 / FP8 MFMA); gemm_common.h holds the operand conventions.
 #include "gemm_common.h"
 
 namespace fp4moe {
+
+// NVFP4 weights x f16 activations, 128-row tiles (gemm_nvf16.hip): block_m
+// 128, fragment weights, K a multiple of 512, output width a multiple of 128
+// (stage 1) or 256 (stage 2).
+void launch_nvf16_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
 
 // ===========================================================================
 // dispatch
@@ -52,11 +58,14 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
                  "fp4_grouped_gemm: NVFP4 weights take bf16 activations (nvfp4_qdq output)");
   // f16 activations: the NVFP4 tiled path only (E2M1 x E4M3 is exact in f16)
   const bool f16a = a->afmt == FP4MOE_A_F16;
-  FP4MOE_REQUIRE(!f16a || (a->wfmt == FP4MOE_W_NVFP4 && a->block_m == 64 &&
+  FP4MOE_REQUIRE(!f16a || (a->wfmt == FP4MOE_W_NVFP4 && (a->block_m == 64 || a->block_m == 128) &&
                            a->w_layout == FP4MOE_LAYOUT_FRAGMENT &&
                            a->a_layout == FP4MOE_A_LAYOUT_ROWMAJOR),
                  "fp4_grouped_gemm: f16 activations need NVFP4 fragment-major weights, block_m "
-                 "64 and row-major A");
+                 "64 or 128 and row-major A");
+  FP4MOE_REQUIRE(!f16a || a->block_m != 128 || a->K % 512 == 0,
+                 "fp4_grouped_gemm: f16 activations with block_m 128 need K a multiple of 512 "
+                 "(K=%d)", a->K);
   FP4MOE_REQUIRE(!f16a || (a->stage == 1 ? a->N / 2 : a->N) % (a->stage == 1 ? 128 : 256) == 0,
                  "fp4_grouped_gemm: f16 activations need an output width that is a multiple "
                  "of 128 (stage 1) or 256 (stage 2)");
@@ -64,7 +73,8 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(a->N > 0 && a->N % 32 == 0 && (a->stage == 2 || a->N % 64 == 0),
                  "fp4_grouped_gemm: N=%d (stage %d)", a->N, a->stage);
   if (dq) {
-    FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64,
+    FP4MOE_REQUIRE(a->block_m == 16 || a->block_m == 32 || a->block_m == 64 ||
+                       (f16a && a->block_m == 128),
                    "fp4_grouped_gemm: block_m=%d not in {16,32,64} for this format pair",
                    a->block_m);
   } else if (mx8 || f8f8) {
@@ -187,6 +197,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   if (mx) launch_mx_gemm(p, st, mt, s);
   else if (mx8) launch_mx_fp8_wide_gemm(p, st, mt, s);
   else if (f8f8) launch_fp8_fp8_wide_gemm(p, st, mt, s);
+  else if (f16a && a->block_m == 128) launch_nvf16_gemm(p, st, mt, s);
   else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");

@@ -86,16 +86,19 @@ class MoELayer:
         self.chunked = (cfg.afmt == "mx" and cfg.fragment_layout and
                         ((cfg.wfmt == "mx" and cfg.block_m in (128, 192, 256)) or
                          (cfg.wfmt == "fp8" and cfg.block_m == 192)))
-        # NVFP4 with 64-row tiles: activations in the f16 operand form of
-        # nvfp4_qdq (E2M1 x E4M3 weights decode to f16 with one packed multiply
-        # per pair, and the 32x32 f16 MFMA runs at twice the 16x16 bf16 rate)
         # W8A8: per-token FP8 activations (chunk-major) x FP8 weights, 128-row tiles
         self.a8 = cfg.afmt == "fp8"
         if self.a8 and not (cfg.wfmt == "fp8" and cfg.block_m == 128 and cfg.fragment_layout):
             raise ValueError("FP8 activations run with FP8 fragment-major weights and block_m 128")
+        # NVFP4 with 64- or 128-row tiles: activations in the f16 operand form
+        # of nvfp4_qdq (E2M1 x E4M3 weights decode to f16 with one conversion
+        # and one packed multiply per pair); the 128-row tiles stream each
+        # weight slice once per 128 rows of its expert and need K % 512 == 0
         n13, n2 = cfg.I, cfg.H
-        self.f16a = (cfg.afmt == "nvfp4" and cfg.wfmt == "nvfp4" and cfg.block_m == 64 and
-                     cfg.fragment_layout and n13 % 128 == 0 and n2 % 256 == 0)
+        self.f16a = (cfg.afmt == "nvfp4" and cfg.wfmt == "nvfp4" and cfg.fragment_layout and
+                     n13 % 128 == 0 and n2 % 256 == 0 and
+                     (cfg.block_m == 64 or
+                      (cfg.block_m == 128 and cfg.H % 512 == 0 and cfg.I % 512 == 0)))
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)

@@ -256,7 +256,7 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * Supported (wfmt, afmt) and block_m:
  *   (MXFP4 | NVFP4 | FP8, BF16) and (FP8, MXFP4) with block_m in {16, 32, 64}:
  *     both operands decoded exactly to bf16 in registers, bf16 MFMA;
- *   (NVFP4, F16) with block_m 64 (see afmt FP4MOE_A_F16 below);
+ *   (NVFP4, F16) with block_m 64 or 128 (see afmt FP4MOE_A_F16 below);
  *   (MXFP4, MXFP4) with block_m in {32, 64, 128, 192, 256}: the gfx950
  *     scaled MFMA, FP4 x FP4, both E8M0 scales as MFMA scale operands;
  *   (FP8, MXFP4) with block_m 192: the gfx950 scaled MFMA in its FP4 x FP8
@@ -290,9 +290,10 @@ int nvfp4_qdq(const uint16_t* x, int M, int K, const int32_t* row_count,
  * are not written.
  * afmt FP4MOE_A_F16 (the f16 operand form of nvfp4_qdq; a_f16_scale points
  * to its power-of-two factor) is taken with NVFP4 fragment-major weights and
- * block_m 64: E2M1 times E4M3 is exact in f16 (at most 6 significant bits,
- * magnitudes 2^-10 .. 2688), so the products equal those of the bf16 form
- * and the factor is applied with the tensor scale in the epilogue.
+ * block_m 64 or 128 (128: K % 512 == 0): E2M1 times E4M3 is exact in f16 (at
+ * most 6 significant bits, magnitudes 2^-10 .. 2688), so the products equal
+ * those of the bf16 form and the factor is applied with the tensor scale in
+ * the epilogue.
  */
 typedef struct {
   int stage;               /* 1 or 2                                                */

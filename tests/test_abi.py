@@ -183,6 +183,12 @@ def test_gemm_rejects_unsupported_combinations():
     assert run(**{**f16, "block_m": 16})[0] == 1
     assert run(**{**f16, "w_layout": 0})[0] == 1
     assert run(**{**f16, "N": 192, "ldo": 96})[0] == 1           # output width 96
+    # block_m 128: the 128-row tiles, K a multiple of 512
+    assert run(**{**f16, "block_m": 128, "K": 512, "lda": 512})[0] == 0
+    assert run(**{**f16, "block_m": 128, "K": 512, "lda": 512, "ldo": 512}, stage=2)[0] == 0
+    st, msg = run(**{**f16, "block_m": 128, "K": 384, "lda": 384})
+    assert st == 1 and "512" in msg
+    assert run(**{**f16, "block_m": 192, "K": 512, "lda": 512})[0] == 1
     assert run(afmt=3)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 

@@ -65,11 +65,12 @@ def routing(rng, T, topk, E, skew=False):
 
 
 def run_stage(gpu_lib, stage, wfmt, afmt, T, topk, E, ns, H, I, bm, seed, skew=False,
-              exact=False, layout=0, a_layout=0, with_f32=True, quant_out=False):
+              exact=False, layout=0, a_layout=0, with_f32=True, quant_out=False, ids=None):
     rng = np.random.default_rng(seed)
     Et = E + ns
     k = topk + ns
-    ids = routing(rng, T, topk, E, skew)
+    if ids is None:
+        ids = routing(rng, T, topk, E, skew)
     perm_ref = OP.moe_permute(ids, E, ns, bm)
     perm = gpu_lib.moe_permute(dev(ids), E, ns, bm)
     n_rows = int(perm_ref["expert_offsets"][-1])
@@ -242,6 +243,39 @@ def test_nvfp4_f16_activation_gemm(gpu_lib, case):
     stage, T, topk, E, ns, H, I, seed, skew = case
     run_stage(gpu_lib, stage, "nvfp4", "f16", T, topk, E, ns, H, I, 64, seed, skew,
               layout=gpu_lib.LAYOUT_FRAGMENT)
+
+
+F16_128_CASES = [
+    # stage, T, topk, E, ns, H, I, seed, skew: NVFP4 weights x f16 activations
+    # in 128-row tiles (K a multiple of 512): hot experts of several tiles with
+    # ragged tails, a shared expert, empty experts, full width, narrow width
+    (1, 300, 4, 8, 0, 512, 512, 71, True),
+    (2, 300, 4, 8, 0, 512, 512, 72, True),
+    (1, 150, 6, 10, 1, 1024, 512, 73, True),
+    (2, 150, 6, 10, 1, 1024, 512, 74, True),
+    (1, 9, 3, 5, 1, 7168, 2048, 75, False),
+    (2, 9, 3, 5, 1, 7168, 2048, 76, False),
+    (1, 40, 2, 6, 0, 512, 128, 77, False),
+    (2, 40, 2, 6, 0, 256, 512, 78, False),
+]
+
+
+@pytest.mark.parametrize("case", F16_128_CASES)
+def test_nvfp4_f16_activation_gemm_128_row_tiles(gpu_lib, case):
+    stage, T, topk, E, ns, H, I, seed, skew = case
+    run_stage(gpu_lib, stage, "nvfp4", "f16", T, topk, E, ns, H, I, 128, seed, skew,
+              layout=gpu_lib.LAYOUT_FRAGMENT)
+
+
+@pytest.mark.parametrize("stage", [1, 2])
+def test_nvfp4_f16_128_row_tiles_every_block_count(gpu_lib, stage):
+    """Expert segments of 1, 33, 70, 127 and 225 rows: tiles with one, two,
+    three and four live 32-row blocks, a full tile, and ragged ends of each."""
+    counts = [1, 33, 70, 127, 225]
+    ids = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = np.random.default_rng(79).permutation(ids)[:, None].astype(np.int32)
+    run_stage(gpu_lib, stage, "nvfp4", "f16", len(ids), 1, len(counts), 0, 512, 512, 128, 80 + stage,
+              layout=gpu_lib.LAYOUT_FRAGMENT, ids=ids)
 
 
 MX_CASES = [

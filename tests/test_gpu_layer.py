@@ -498,9 +498,11 @@ def test_layer_fp8_full_size_sampled(gpu_lib):
     _full_size_layer(gpu_lib, "skewed", "fp8", 13)
 
 
-def test_layer_nvfp4_full_size_sampled(gpu_lib):
+@pytest.mark.parametrize("bm", [128, 64])
+def test_layer_nvfp4_full_size_sampled(gpu_lib, bm):
     """The NVFP4 emulation layer at the benchmarked size and launch configuration
-    (T=2048, 64-row tiles, activations in the f16 operand form), stage by stage
+    (T=2048, 128-row tiles; also 64-row tiles; activations in the f16 operand
+    form), stage by stage
     on the GPU's own upstream outputs (the second QDQ's tensor scale spans all
     of h and couples every token, so each stage is checked on what the GPU fed
     it):
@@ -524,18 +526,19 @@ def test_layer_nvfp4_full_size_sampled(gpu_lib):
     bias = synth.router_bias(w)
     xb = synth.activations(w, T, 0)
     rid, rw = OR.moe_route(logits, bias, w.n_group, w.topk_group, w.topk)
-    perm = OP.moe_permute(rid, w.E, w.n_shared, 64)
+    perm = OP.moe_permute(rid, w.E, w.n_shared, bm)
     offs = perm["expert_offsets"]
     counts = np.diff(offs)
     n_rows = int(offs[-1])
     # sampled sorted rows: the first and last rows of the most loaded expert
-    # and of its first and last 64-row tiles, both ends of a one-tile expert,
-    # a one-row expert if any, and random rows
+    # and of its first and last tiles, both ends of a one-tile expert, a
+    # one-row expert if any, and random rows
     g = np.random.default_rng(98)
     big = int(np.argmax(counts))
     lo, hi = int(offs[big]), int(offs[big + 1])
-    rows = [lo, lo + 63, lo + 64, hi - 65, hi - 64, hi - 1]
-    one = np.flatnonzero((counts > 1) & (counts <= 64))
+    last0 = lo + (hi - lo - 1) // bm * bm          # first row of the last tile
+    rows = [lo, lo + bm - 1, lo + bm, last0 - 1, last0, hi - 1]
+    one = np.flatnonzero((counts > 1) & (counts <= bm))
     if one.size:
         rows += [int(offs[one[0]]), int(offs[one[0] + 1]) - 1]
     single = np.flatnonzero(counts == 1)
@@ -563,8 +566,9 @@ def test_layer_nvfp4_full_size_sampled(gpu_lib):
     dev_w["w13_ts"], dev_w["w2_ts"] = dev(ts["w13"]), dev(ts["w2"])
     cfg = gpu_lib.LayerConfig(H=H, I=I, E=w.E, n_shared=w.n_shared, n_group=w.n_group,
                               topk_group=w.topk_group, topk=w.topk, afmt="nvfp4", wfmt="nvfp4",
-                              block_m=64)
+                              block_m=bm)
     layer = gpu_lib.MoELayer(cfg, dev_w)
+    assert layer.f16a, "the f16 operand path"
     del dev_w
     b = layer.forward(bf16_dev(xb), dev(logits), dev(bias), keep=True)
     assert_equal(host(b["topk_ids"]), rid, "topk_ids")
@@ -633,14 +637,15 @@ def test_layer_prefill_is_deterministic(gpu_lib):
     _twice(gpu_lib, synth.WORKLOADS["prefill"], 24, "mx", "mx", 192)
 
 
-@pytest.mark.parametrize("block_m", [16, 64])
+@pytest.mark.parametrize("block_m", [16, 64, 128])
 def test_layer_nvfp4_full_width(gpu_lib, block_m):
     run_layer(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", block_m)
 
 
-def test_layer_nvfp4_is_deterministic(gpu_lib):
+@pytest.mark.parametrize("block_m", [64, 128])
+def test_layer_nvfp4_is_deterministic(gpu_lib, block_m):
     """The NVFP4 tensor amax is an atomic maximum (order-free); the rest has no atomics."""
-    _twice(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", 64)
+    _twice(gpu_lib, synth.WORKLOADS["nvfp4"], 6, "nvfp4", "nvfp4", block_m)
 
 
 @pytest.mark.parametrize("block_m", [32, 64, 192])
