@@ -67,6 +67,7 @@ class GemmArgs(ctypes.Structure):
         ("w_layout", ctypes.c_int), ("a_layout", ctypes.c_int), ("a_rows", ctypes.c_int),
         ("out_q", ctypes.c_void_p), ("out_q_scale", ctypes.c_void_p), ("out_q_rows", ctypes.c_int),
         ("a_f16_scale", ctypes.c_void_p), ("a_row_scale", ctypes.c_void_p),
+        ("work_queue", ctypes.c_void_p),
     ]
 
 
@@ -294,7 +295,7 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                      w_tensor_scale=None, w_channel_scale=None, a_row_gather=None,
                      gather_div=1, out=None, out_f32=None, max_rows=None, w_layout=0,
                      a_layout=0, out_q=None, out_q_scale=None, no_out=False, a_f16_scale=None,
-                     a_row_scale=None, stream=None):
+                     a_row_scale=None, work_queue=None, stream=None):
     """One GEMM stage over the expert segments described by `perm` (moe_permute output).
 
     w: weight codes [E, N, K/2] (FP8: [E, N, K]); a: bf16 [rows, K] or MXFP4
@@ -304,6 +305,8 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
     and a_f16_scale its float32 [1] power-of-two factor.
     afmt A_FP8 (FP8 weights, block_m 128): a is fp8_quant_per_token's chunk-major
     E4M3 codes [K/128, rows, 128] and a_row_scale its float32 [rows] scales.
+    work_queue (A_F16 at block_m 128): an int32 [16] tensor, zero-filled once;
+    the workgroups then take their items from it as they free up.
     out_q / out_q_scale (stage 1, block_m 192): chunk-major MXFP4 copies of the
     output [N_out/128, rows, 64] / [N_out/128, rows, 4]; with no_out=True the
     bf16 output is not written (returns None).
@@ -341,7 +344,8 @@ def fp4_grouped_gemm(stage, wfmt, afmt, w, w_scale, a, perm, block_m, *, a_scale
                     None if out_q_scale is None else out_q_scale.data_ptr(),
                     0 if out_q is None else out_q.shape[1],
                     None if a_f16_scale is None else a_f16_scale.data_ptr(),
-                    None if a_row_scale is None else a_row_scale.data_ptr())
+                    None if a_row_scale is None else a_row_scale.data_ptr(),
+                    None if work_queue is None else work_queue.data_ptr())
     _check(lib.fp4_grouped_gemm(ctypes.byref(args), _stream(stream)))
     return out
 

@@ -8,8 +8,8 @@ namespace fp4moe {
 
 // NVFP4 weights x f16 activations, 128-row tiles (gemm_nvf16.hip): block_m
 // 128, fragment weights, K a multiple of 512, output width a multiple of 128
-// (stage 1) or 256 (stage 2).
-void launch_nvf16_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s);
+// (stage 1) or 256 (stage 2); `queue` (optional) the work queue.
+void launch_nvf16_gemm(const GemmParams& p, int stage, int max_tiles, int* queue, hipStream_t s);
 
 // ===========================================================================
 // dispatch
@@ -66,6 +66,8 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   FP4MOE_REQUIRE(!f16a || a->block_m != 128 || a->K % 512 == 0,
                  "fp4_grouped_gemm: f16 activations with block_m 128 need K a multiple of 512 "
                  "(K=%d)", a->K);
+  FP4MOE_REQUIRE(((uintptr_t)a->work_queue & 3) == 0,
+                 "fp4_grouped_gemm: work_queue must be 4-byte aligned");
   FP4MOE_REQUIRE(!f16a || (a->stage == 1 ? a->N / 2 : a->N) % (a->stage == 1 ? 128 : 256) == 0,
                  "fp4_grouped_gemm: f16 activations need an output width that is a multiple "
                  "of 128 (stage 1) or 256 (stage 2)");
@@ -197,7 +199,7 @@ extern "C" int fp4_grouped_gemm(const fp4moe_gemm_args* a, void* stream) {
   if (mx) launch_mx_gemm(p, st, mt, s);
   else if (mx8) launch_mx_fp8_wide_gemm(p, st, mt, s);
   else if (f8f8) launch_fp8_fp8_wide_gemm(p, st, mt, s);
-  else if (f16a && a->block_m == 128) launch_nvf16_gemm(p, st, mt, s);
+  else if (f16a && a->block_m == 128) launch_nvf16_gemm(p, st, mt, a->work_queue, s);
   else if (dqt_supported(p, st)) launch_dqt_gemm(p, a->wfmt, a->afmt, st, mt, s);
   else launch_dq_gemm(p, a->wfmt, a->afmt, st, mt, s);
   return check_launch("fp4_grouped_gemm");

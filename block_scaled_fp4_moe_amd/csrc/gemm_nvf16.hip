@@ -211,26 +211,94 @@ __device__ __forceinline__ void nv_item(const GemmParams& p, uint8_t* smem, int 
   }
 }
 
+// Cost of a tile's items for the split of the work between XCDs: a workgroup
+// spends about as much per item on streaming and decoding its weight slice
+// as on one 32-row block of MFMAs, so live blocks plus one.
+__device__ inline int nv_tile_cost(const GemmParams& p, int t) {
+  const int e = p.tiles[2 * t], mt = p.tiles[2 * t + 1];
+  int rows = p.offsets[e + 1] - p.offsets[e] - mt * NV_BM;
+  rows = rows < NV_BM ? rows : NV_BM;
+  return (rows + 31) / 32 + 1;
+}
+
+// The tile-list split point of XCD x (0..8): the first tile at which the
+// running cost reaches x/8 of the total, moved back to the first tile of its
+// expert (an expert's tiles share their weight slices under one L2).  Wave 0
+// computes it; every lane returns it.
+__device__ inline int nv_split(const GemmParams& p, int n_tiles, int x, int lane) {
+  const int per_lane = (n_tiles + 63) / 64;
+  const int t0 = min(n_tiles, lane * per_lane), t1 = min(n_tiles, t0 + per_lane);
+  int sum = 0;
+  for (int t = t0; t < t1; ++t) sum += nv_tile_cost(p, t);
+  int incl = sum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int total = __shfl(incl, 63);
+  int bt = n_tiles;
+  if (x < 8) {
+    const int64_t target = (int64_t)total * x / 8;
+    int run = incl - sum;
+    for (int t = t0; t < t1; ++t) {
+      if (run >= target) { bt = t; break; }
+      run += nv_tile_cost(p, t);
+    }
+  }
+  for (int d = 32; d >= 1; d >>= 1) bt = min(bt, __shfl_xor(bt, d));
+  return bt < n_tiles ? bt - p.tiles[2 * bt + 1] : n_tiles;
+}
+
+// Work items are (M tile, column block) pairs, in (column block, M tile)
+// order inside an expert: the M tiles that share a weight slice, and the
+// column blocks of a single-tile expert that share an activation tile, are
+// neighbours and run side by side.  Each XCD (workgroups blockIdx % 8) takes
+// a contiguous range of the list.  Without a queue the range is an equal
+// share of the items and its workgroups take every slots-th item; with a
+// queue the range is an equal share of the cost and its workgroups take the
+// next item from the XCD's counter as they free up (item costs differ up to
+// fivefold with the live-block count), and the last workgroup out returns
+// every counter to zero.
 template <int STAGE, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void nvf16_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(64 * NW, 1) void nvf16_gemm_kernel(GemmParams p, int* queue) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[NV_STAGES * NV_STAGE_BYTES];
+  __shared__ int s_split[2];
+  __shared__ int s_item;
   constexpr int OUT_PER_WG = (STAGE == 1 ? 32 : 64) * NW;
   const int n_out = STAGE == 1 ? p.N / 2 : p.N;
   const int n_nb = n_out / OUT_PER_WG;
-  const int64_t n_work = (int64_t)(*p.n_tiles) * n_nb;
+  const int n_tiles = *p.n_tiles;
+  const int tid = threadIdx.x;
 
-  // Each XCD (workgroups blockIdx % 8) takes a contiguous range of the work:
-  // the M tiles of one expert that share a weight slice run side by side
-  // under one L2.
   constexpr int NX = 8;
   const int xcd = blockIdx.x % NX, slot = blockIdx.x / NX;
   const int slots = ((int)gridDim.x - xcd + NX - 1) / NX;
-  const int64_t per = (n_work + NX - 1) / NX;
-  const int64_t w_begin = (int64_t)xcd * per;
-  const int64_t w_end = min(n_work, w_begin + per);
+  int64_t w_begin, w_end;
+  if (queue) {
+    if (tid < 64) {
+      const int b0 = nv_split(p, n_tiles, xcd, tid);
+      const int b1 = nv_split(p, n_tiles, xcd + 1, tid);
+      if (tid == 0) s_split[0] = b0, s_split[1] = b1;
+    }
+    __syncthreads();
+    w_begin = (int64_t)s_split[0] * n_nb;
+    w_end = (int64_t)s_split[1] * n_nb;
+  } else {
+    const int64_t n_work = (int64_t)n_tiles * n_nb;
+    const int64_t per = (n_work + NX - 1) / NX;
+    w_begin = (int64_t)xcd * per;
+    w_end = min(n_work, w_begin + per);
+  }
 
-  for (int64_t wi = w_begin + slot; wi < w_end; wi += slots) {
-    // (column block, M tile) order inside an expert
+  for (int64_t k = slot;; k += slots) {
+    int64_t wi = w_begin + k;
+    if (queue) {
+      __syncthreads();                      // every wave has read the previous item
+      if (tid == 0) s_item = atomicAdd(queue + xcd, 1);
+      __syncthreads();
+      wi = w_begin + s_item;
+    }
+    if (wi >= w_end) break;
     const int any_tile = (int)(wi / n_nb);
     const int e = p.tiles[2 * any_tile];
     const int t0 = any_tile - p.tiles[2 * any_tile + 1];
@@ -246,30 +314,39 @@ __global__ __launch_bounds__(64 * NW, 1) void nvf16_gemm_kernel(GemmParams p) {
       default: nv_item<STAGE, NW, 4>(p, smem, e, nb, tile_row0, row_end); break;
     }
   }
+  // Every workgroup's last (empty) take precedes its arrival; the last to
+  // arrive zeroes the counters for the next call on the queue.
+  if (queue && tid == 0) {
+    __threadfence();
+    if (atomicAdd(queue + NX, 1) == (int)gridDim.x - 1) {
+      __threadfence();
+      for (int i = 0; i <= NX; ++i) atomicExch(queue + i, 0);
+    }
+  }
 }
 
 }  // namespace
 
 template <int STAGE, int NW>
-static void launch_nvf16_stage(const GemmParams& p, int max_tiles, hipStream_t s) {
+static void launch_nvf16_stage(const GemmParams& p, int max_tiles, int* queue, hipStream_t s) {
   const int n_out = STAGE == 1 ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / ((STAGE == 1 ? 32 : 64) * NW));
   const int cap = grid_cap() / 8;        // one workgroup per CU
   const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
-  hipLaunchKernelGGL((nvf16_gemm_kernel<STAGE, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+  hipLaunchKernelGGL((nvf16_gemm_kernel<STAGE, NW>), dim3(grid), dim3(64 * NW), 0, s, p, queue);
 }
 
 // Eight waves (two per SIMD: a tile 512 weight rows wide, half the activation
 // reads per weight of four waves) when the output width allows, else four.
-void launch_nvf16_gemm(const GemmParams& p, int stage, int max_tiles, hipStream_t s) {
+void launch_nvf16_gemm(const GemmParams& p, int stage, int max_tiles, int* queue, hipStream_t s) {
   const int n_out = stage == 1 ? p.N / 2 : p.N;
   const bool eight = n_out % (stage == 1 ? 256 : 512) == 0;
   if (stage == 1) {
-    if (eight) launch_nvf16_stage<1, 8>(p, max_tiles, s);
-    else launch_nvf16_stage<1, 4>(p, max_tiles, s);
+    if (eight) launch_nvf16_stage<1, 8>(p, max_tiles, queue, s);
+    else launch_nvf16_stage<1, 4>(p, max_tiles, queue, s);
   } else {
-    if (eight) launch_nvf16_stage<2, 8>(p, max_tiles, s);
-    else launch_nvf16_stage<2, 4>(p, max_tiles, s);
+    if (eight) launch_nvf16_stage<2, 8>(p, max_tiles, queue, s);
+    else launch_nvf16_stage<2, 4>(p, max_tiles, queue, s);
   }
 }
 

@@ -102,6 +102,10 @@ class MoELayer:
         self.device = device
         self._bufs = {}
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
+        # the 128-row NVFP4 tiles take their items from a work queue (zero-filled
+        # once; every call leaves it so; both stages run in order on one stream)
+        self.gemm_queue = (torch.zeros(16, dtype=torch.int32, device=device)
+                           if self.f16a and cfg.block_m == 128 else None)
         # the single-launch decode: bf16 activations, fragment-major MXFP4
         # weights, 16-row tiles (its workspace is zero-filled once, here)
         self.fused_ok = (cfg.fused_decode and cfg.afmt == "bf16" and cfg.wfmt == "mx" and
@@ -232,7 +236,7 @@ class MoELayer:
         # then written only when the caller keeps the intermediates)
         fused_q = self.chunked and c.block_m == 192
         qkw = dict(out_q=b["hq"], out_q_scale=b["hs"], no_out=not keep) if fused_q else {}
-        f16kw = dict(a_f16_scale=b["xs"]) if self.f16a else {}
+        f16kw = dict(a_f16_scale=b["xs"], work_queue=self.gemm_queue) if self.f16a else {}
         if self.a8:
             f16kw = dict(a_row_scale=b["xs"])
         fp4_grouped_gemm(1, wf, af, w["w13"], None if c.wfmt == "fp8" else w["w13_scale"], a1,
@@ -268,7 +272,7 @@ class MoELayer:
         ts2 = w.get("w2_ts") if c.wfmt == "nvfp4" else None
         cs2 = w["w2_scale"] if c.wfmt == "fp8" else None
         tick("stage2")
-        f16kw = dict(a_f16_scale=b["hs"]) if self.f16a else {}
+        f16kw = dict(a_f16_scale=b["hs"], work_queue=self.gemm_queue) if self.f16a else {}
         if self.a8:
             f16kw = dict(a_row_scale=b["hs"])
         fp4_grouped_gemm(2, wf, af, w["w2"], None if c.wfmt == "fp8" else w["w2_scale"], a2, perm,

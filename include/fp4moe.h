@@ -328,6 +328,13 @@ typedef struct {
   int out_q_rows;          /*   rows per K chunk slab of out_q / out_q_scale        */
   const float* a_f16_scale;  /* FP4MOE_A_F16: device [1], the power-of-two factor   */
   const float* a_row_scale;  /* FP4MOE_A_FP8: device [a_rows], one scale per row of a */
+  int32_t* work_queue;     /* optional, (NVFP4, F16) at block_m 128: device int32 [16],
+                              zero-filled once before its first use; every call leaves
+                              it zero-filled.  Given, the workgroups take their items
+                              from it as they free up (balanced by row count) instead
+                              of a fixed share; calls sharing one queue must not
+                              overlap (order them on one stream).  Other format pairs
+                              ignore it.  NULL: the fixed share.                      */
 } fp4moe_gemm_args;
 
 int fp4_grouped_gemm(const fp4moe_gemm_args* args, void* stream);

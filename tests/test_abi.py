@@ -111,7 +111,7 @@ def test_gemm_rejects_unsupported_combinations():
                            None, a["ldo"], a.get("out_f32"), a.get("w_layout", 0),
                            a.get("a_layout", 0), a.get("a_rows", 0), a.get("out_q"),
                            a.get("out_q_scale"), a.get("out_q_rows", 0), a.get("a_f16_scale"),
-                           a.get("a_row_scale"))
+                           a.get("a_row_scale"), a.get("work_queue"))
         return _status(lambda lib: lib.fp4_grouped_gemm(ctypes.byref(args), None))
     assert run(stage=3)[0] == 1
     assert run(wfmt=1, afmt=1)[0] == 1          # NVFP4 weights need bf16 activations
@@ -189,6 +189,10 @@ def test_gemm_rejects_unsupported_combinations():
     st, msg = run(**{**f16, "block_m": 128, "K": 384, "lda": 384})
     assert st == 1 and "512" in msg
     assert run(**{**f16, "block_m": 192, "K": 512, "lda": 512})[0] == 1
+    # the work queue: any 4-byte aligned device pointer (never touched here)
+    assert run(**{**f16, "block_m": 128, "K": 512, "lda": 512}, work_queue=256)[0] == 0
+    st, msg = run(**{**f16, "block_m": 128, "K": 512, "lda": 512}, work_queue=258)
+    assert st == 1 and "work_queue" in msg
     assert run(afmt=3)[0] == 1
     assert run(max_tiles=0)[0] == 0             # nothing to do: OK without touching pointers
 

@@ -268,6 +268,39 @@ def test_nvfp4_f16_activation_gemm_128_row_tiles(gpu_lib, case):
 
 
 @pytest.mark.parametrize("stage", [1, 2])
+def test_nvfp4_f16_128_row_tiles_work_queue(gpu_lib, stage):
+    """With a work queue the workgroups take their items as they free up: the
+    same bytes as the fixed share (every item is computed the same way), on
+    two calls in a row, the second with fewer rows, and the queue zero-filled
+    after each call."""
+    rng = np.random.default_rng(90 + stage)
+    E, topk, H, I = 12, 4, 1024, 512
+    N, K = (2 * I, H) if stage == 1 else (H, I)
+    wd = make_weights(rng, E, N, K, "nvfp4")
+    wc, ws = gpu_lib.fp4_weight_preshuffle(gpu_lib.W_NVFP4, dev(wd["codes"]), dev(wd["scale"]))
+    queue = torch.zeros(16, dtype=torch.int32, device="cuda")
+    for T in (400, 90):
+        ids = routing(rng, T, topk, E, skew=True)
+        perm = gpu_lib.moe_permute(dev(ids), E, 0, 128)
+        rows_in = T if stage == 1 else T * topk
+        a16 = (rng.integers(-6, 7, (rows_in, K)) * 0.25).astype(np.float16)
+        a = dev(a16.view(np.int16)).view(torch.float16)
+        kw = dict(a_f16_scale=dev(np.array([1.0], np.float32)), w_tensor_scale=dev(wd["ts"]),
+                  w_layout=gpu_lib.LAYOUT_FRAGMENT)
+        if stage == 1:
+            kw.update(a_row_gather=perm["sorted_pairs"], gather_div=topk)
+        outs = []
+        for q in (None, queue):
+            o = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.W_NVFP4, gpu_lib.A_F16, wc, ws, a, perm,
+                                         128, work_queue=q, **kw)
+            torch.cuda.synchronize()
+            outs.append(bits_of(o)[: int(host(perm["expert_offsets"])[-1])].copy())
+            if q is not None:
+                assert not host(q).any(), "queue left non-zero"
+        assert outs[0].tobytes() == outs[1].tobytes(), f"T={T}: queue and fixed share differ"
+
+
+@pytest.mark.parametrize("stage", [1, 2])
 def test_nvfp4_f16_128_row_tiles_every_block_count(gpu_lib, stage):
     """Expert segments of 1, 33, 70, 127 and 225 rows: tiles with one, two,
     three and four live 32-row blocks, a full tile, and ragged ends of each."""
