@@ -281,8 +281,9 @@ __global__ __launch_bounds__(64 * NW, 1) void nvf16_gemm_kernel(GemmParams p, in
       if (tid == 0) s_split[0] = b0, s_split[1] = b1;
     }
     __syncthreads();
-    w_begin = (int64_t)s_split[0] * n_nb;
-    w_end = (int64_t)s_split[1] * n_nb;
+    // (wave-uniform: held in scalar registers)
+    w_begin = (int64_t)__builtin_amdgcn_readfirstlane(s_split[0]) * n_nb;
+    w_end = (int64_t)__builtin_amdgcn_readfirstlane(s_split[1]) * n_nb;
   } else {
     const int64_t n_work = (int64_t)n_tiles * n_nb;
     const int64_t per = (n_work + NX - 1) / NX;
@@ -296,7 +297,7 @@ __global__ __launch_bounds__(64 * NW, 1) void nvf16_gemm_kernel(GemmParams p, in
       __syncthreads();                      // every wave has read the previous item
       if (tid == 0) s_item = atomicAdd(queue + xcd, 1);
       __syncthreads();
-      wi = w_begin + s_item;
+      wi = w_begin + __builtin_amdgcn_readfirstlane(s_item);
     }
     if (wi >= w_end) break;
     const int any_tile = (int)(wi / n_nb);
