@@ -341,9 +341,9 @@ extern "C" int moe_decode_fused(const fp4moe_decode_args* a, void* stream) {
   const int max_tiles = moe_permute_max_tiles(a->T, a->topk, a->E, a->n_shared, kFusedBM);
   FP4MOE_REQUIRE(a->max_tiles >= max_tiles, "moe_decode_fused: max_tiles=%d < %d",
                  a->max_tiles, max_tiles);
-  FP4MOE_REQUIRE(a->workspace_bytes >= moe_decode_fused_workspace(a->H),
-                 "moe_decode_fused: workspace %zu < %zu bytes", a->workspace_bytes,
-                 moe_decode_fused_workspace(a->H));
+  if (a->workspace_bytes < moe_decode_fused_workspace(a->H))
+    return set_error(FP4MOE_ERR_WORKSPACE, "moe_decode_fused: workspace %zu < %zu bytes",
+                     a->workspace_bytes, moe_decode_fused_workspace(a->H));
   if (a->T == 0) return FP4MOE_OK;
   FP4MOE_REQUIRE(a->x && a->logits && a->w13 && a->w13_scale && a->w2 && a->w2_scale &&
                      a->topk_ids && a->topk_w && a->expert_offsets && a->sorted_pairs &&

@@ -274,13 +274,15 @@ def _decode_args(**kw):
                                  dict(max_tiles=8), dict(workspace_bytes=16)])
 def test_decode_fused_rejects_bad_arguments(bad):
     """Argument and workspace checks of the single-launch decode, before any
-    device work (the pointers are never dereferenced)."""
+    device work (the pointers are never dereferenced): FP4MOE_ERR_INVALID_ARG,
+    or FP4MOE_ERR_WORKSPACE for a workspace below moe_decode_fused_workspace."""
     lib = fm.load()
     ws = lib.moe_decode_fused_workspace(7168)
     assert ws == (4 + 112) * 4
     a = _decode_args(**{"workspace_bytes": ws, **bad})
     st, msg = _status(lambda lib: lib.moe_decode_fused(ctypes.byref(a), None))
-    assert st == 1 and "moe_decode_fused" in msg, (bad, st, msg)
+    want = 3 if "workspace_bytes" in bad else 1
+    assert st == want and "moe_decode_fused" in msg, (bad, st, msg)
     # T = 0 with valid sizes is accepted and does nothing
     a = _decode_args(T=0, max_tiles=0, workspace_bytes=ws)
     assert _status(lambda lib: lib.moe_decode_fused(ctypes.byref(a), None))[0] == 0
