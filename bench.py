@@ -17,6 +17,9 @@ working set.
 
 Also reported on the same line:
   decode_sweep  the same layer at T = 1 and 64
+  decode_expert_scaling
+                each decode GEMM stage alone against the number of touched
+                experts (one row each), the items-per-compute-unit picture
   prefill       T = 8192, uniform routing, MXFP4 activations and the gfx950
                 scaled FP4 x FP4 MFMA: TFLOP/s = 88,080,384 FLOP per
                 (token, expert) pair
@@ -266,6 +269,61 @@ def run_decode(fm, w, dev_w, T, steps, warmup, torch, args, fused=False):
               + json.dumps({k2: round(v * 1e3, 1) for k2, v in r['per_kernel_ms'].items()})
               + ", step spread " + json.dumps(r["spread"]))
     return r
+
+
+def run_expert_scaling(fm, w, dev_w, torch, args, counts=(1, 2, 4, 8, 9, 12, 16, 32)):
+    """Each decode GEMM stage alone with one row on each of n routed experts
+    (n = 9 is the T=1 layer: 8 routed + the shared expert), 32 disjoint expert
+    sets rotated so that no weight byte is reused from the caches.  Shows how
+    the time follows the bytes each compute unit streams: the work items
+    (16-row tile x 32 output columns in stage 1, x 64 in stage 2) are spread
+    over the 256 compute units, and one unit alone streams about 20-25 GB/s."""
+    H, I, E = w.H, w.I, w.E
+    x = batch_inputs(w, 32, 77, torch)[0]
+    h = x[:, :I].contiguous()
+    hb = torch.empty(32, I, dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty(32, H, dtype=torch.bfloat16, device="cuda")
+
+    def timed(calls, reps=3):
+        for c in calls[:4]:
+            c()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for c in calls:
+                c()
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / len(calls)
+            best = us if best is None else min(best, us)
+        return best
+
+    rows = []
+    for n in counts:
+        perms = []
+        for r in range(32):
+            ids = torch.tensor([[(r * 12 + j * 41) % E] for j in range(n)], dtype=torch.int32,
+                               device="cuda")
+            perms.append(fm.moe_permute(ids, E, 0, 16))
+        s1 = [lambda p=p: fm.fp4_grouped_gemm(1, fm.W_MXFP4, fm.A_BF16, dev_w["w13"],
+                                              dev_w["w13_scale"], x, p, 16,
+                                              a_row_gather=p["sorted_pairs"], gather_div=1,
+                                              out=hb, w_layout=fm.LAYOUT_FRAGMENT) for p in perms]
+        s2 = [lambda p=p: fm.fp4_grouped_gemm(2, fm.W_MXFP4, fm.A_BF16, dev_w["w2"],
+                                              dev_w["w2_scale"], h, p, 16, out=yb,
+                                              w_layout=fm.LAYOUT_FRAGMENT) for p in perms]
+        t1, t2 = timed(s1), timed(s2)
+        rows.append(dict(experts=n, stage1_us=round(t1, 2),
+                         stage1_gbs=round(n * BYTES_W13 / (t1 * 1e3), 1),
+                         stage1_items_per_cu=round(n * (I // 32) / 256, 3),
+                         stage2_us=round(t2, 2),
+                         stage2_gbs=round(n * BYTES_W2 / (t2 * 1e3), 1),
+                         stage2_items_per_cu=round(n * (H // 64) / 256, 3)))
+        log(args, "expert scaling " + json.dumps(rows[-1]))
+    return rows
 
 
 EP_RANKS = 8
@@ -705,8 +763,10 @@ def main():
                                   kernels_us={k2: round(v * 1e3, 2)
                                               for k2, v in r["per_kernel_ms"].items()})
     ep = None
+    scaling = None
     if not args.no_sweep:
         ep = run_ep_share(fm, w, dev_w, args.tokens, args.steps, args.warmup, torch, args)
+        scaling = run_expert_scaling(fm, w, dev_w, torch, args)
     prefill = None
     if not args.no_prefill:
         r = run_prefill(fm, dev_w, args.prefill_steps, torch, args)
@@ -780,6 +840,7 @@ def main():
         "decode_sweep": sweep,
         "decode_single_launch": single,
         "ep_share": ep,
+        "decode_expert_scaling": scaling,
         "prefill": prefill,
         "skewed_prefill": skewed,
         "nvfp4": extra.get("nvfp4"),
