@@ -333,7 +333,11 @@ static void launch_nvf16_stage(const GemmParams& p, int max_tiles, int* queue, h
   const int n_out = STAGE == 1 ? p.N / 2 : p.N;
   const int64_t work = (int64_t)max_tiles * (n_out / ((STAGE == 1 ? 32 : 64) * NW));
   const int cap = grid_cap() / 8;        // one workgroup per CU
-  const int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
+  int grid = (int)(work < cap ? (work < 1 ? 1 : work) : cap);
+  // With a queue the items are split between the eight XCD groups by cost,
+  // so any group may own items however few there are: every group needs a
+  // workgroup (the fixed share gives group x items only when x < work).
+  if (queue && grid < 8) grid = 8;
   hipLaunchKernelGGL((nvf16_gemm_kernel<STAGE, NW>), dim3(grid), dim3(64 * NW), 0, s, p, queue);
 }
 

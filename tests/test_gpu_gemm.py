@@ -267,19 +267,25 @@ def test_nvfp4_f16_activation_gemm_128_row_tiles(gpu_lib, case):
               layout=gpu_lib.LAYOUT_FRAGMENT)
 
 
-@pytest.mark.parametrize("stage", [1, 2])
-def test_nvfp4_f16_128_row_tiles_work_queue(gpu_lib, stage):
+@pytest.mark.parametrize("stage,E,topk,H,I,Ts", [
+    (1, 12, 4, 1024, 512, (400, 90)),
+    (2, 12, 4, 1024, 512, (400, 90)),
+    # fewer items than the eight XCD groups the cost split serves (one or two
+    # column blocks, a handful of tiles)
+    (1, 6, 1, 512, 512, (3, 5, 1)),
+    (2, 6, 1, 512, 512, (3, 5, 1)),
+])
+def test_nvfp4_f16_128_row_tiles_work_queue(gpu_lib, stage, E, topk, H, I, Ts):
     """With a work queue the workgroups take their items as they free up: the
     same bytes as the fixed share (every item is computed the same way), on
-    two calls in a row, the second with fewer rows, and the queue zero-filled
-    after each call."""
-    rng = np.random.default_rng(90 + stage)
-    E, topk, H, I = 12, 4, 1024, 512
+    calls in a row with different row counts, and the queue zero-filled after
+    each call."""
+    rng = np.random.default_rng(90 + stage + H)
     N, K = (2 * I, H) if stage == 1 else (H, I)
     wd = make_weights(rng, E, N, K, "nvfp4")
     wc, ws = gpu_lib.fp4_weight_preshuffle(gpu_lib.W_NVFP4, dev(wd["codes"]), dev(wd["scale"]))
     queue = torch.zeros(16, dtype=torch.int32, device="cuda")
-    for T in (400, 90):
+    for T in Ts:
         ids = routing(rng, T, topk, E, skew=True)
         perm = gpu_lib.moe_permute(dev(ids), E, 0, 128)
         rows_in = T if stage == 1 else T * topk
@@ -291,12 +297,16 @@ def test_nvfp4_f16_128_row_tiles_work_queue(gpu_lib, stage):
             kw.update(a_row_gather=perm["sorted_pairs"], gather_div=topk)
         outs = []
         for q in (None, queue):
-            o = gpu_lib.fp4_grouped_gemm(stage, gpu_lib.W_NVFP4, gpu_lib.A_F16, wc, ws, a, perm,
-                                         128, work_queue=q, **kw)
+            # rows never written would keep this pattern (a NaN in bf16)
+            o = torch.full((T * topk, N // 2 if stage == 1 else N), -1, dtype=torch.int16,
+                           device="cuda").view(torch.bfloat16)
+            gpu_lib.fp4_grouped_gemm(stage, gpu_lib.W_NVFP4, gpu_lib.A_F16, wc, ws, a, perm,
+                                     128, work_queue=q, out=o, **kw)
             torch.cuda.synchronize()
             outs.append(bits_of(o)[: int(host(perm["expert_offsets"])[-1])].copy())
             if q is not None:
                 assert not host(q).any(), "queue left non-zero"
+        assert not (outs[0] == 0xFFFF).any(), f"T={T}: rows left unwritten"
         assert outs[0].tobytes() == outs[1].tobytes(), f"T={T}: queue and fixed share differ"
 
 
