@@ -12,6 +12,7 @@ Every step is a kernel of libfp4moe; this module only allocates device
 buffers (once per token count) and passes pointers.
 """
 
+from collections import OrderedDict
 from dataclasses import dataclass
 
 import torch
@@ -31,6 +32,10 @@ ROUTE_PERMUTE_MAX_TOKENS = 8
 
 # moe_decode_fused (the whole layer in one launch) takes at most 16 tokens.
 FUSED_DECODE_MAX_TOKENS = 16
+
+# Intermediate buffers are kept per batch size for reuse; the least recently
+# used sizes beyond this many are released (a serving loop sees many sizes).
+MAX_CACHED_BATCH_SIZES = 8
 
 
 @dataclass
@@ -100,7 +105,7 @@ class MoELayer:
                      (cfg.block_m == 64 or
                       (cfg.block_m == 128 and cfg.H % 512 == 0 and cfg.I % 512 == 0)))
         self.device = device
-        self._bufs = {}
+        self._bufs = OrderedDict()
         self.nvfp4_ws = torch.empty(256, dtype=torch.uint8, device=device)
         # the 128-row NVFP4 tiles take their items from a work queue (zero-filled
         # once; every call leaves it so; both stages run in order on one stream)
@@ -119,6 +124,7 @@ class MoELayer:
 
     def _buffers(self, T):
         if T in self._bufs:
+            self._bufs.move_to_end(T)
             return self._bufs[T]
         c = self.cfg
         k = c.topk + c.n_shared
@@ -163,6 +169,8 @@ class MoELayer:
             b["xs"] = torch.empty(1, dtype=torch.float32, device=dev)
             b["hs"] = torch.empty(1, dtype=torch.float32, device=dev)
         self._bufs[T] = b
+        while len(self._bufs) > MAX_CACHED_BATCH_SIZES:
+            self._bufs.popitem(last=False)
         return b
 
     def forward(self, x, logits, bias, keep=False, stream=None, events=None):

@@ -298,3 +298,20 @@ def test_fp8_quant_rejects_bad_arguments():
         assert st == 1 and "fp8_quant_per_token" in msg, (M, K, ldx, out_rows, msg)
     assert _status(lambda lib: lib.fp8_quant_per_token(None, 0, 256, 256, None, 0, None, None,
                                                        None))[0] == 0
+
+
+def test_layer_buffer_cache_is_bounded():
+    """The layer keeps its intermediate buffers for the most recently used
+    batch sizes only (host-side sizing; the buffers live on the CPU here)."""
+    from block_scaled_fp4_moe_amd import layer as L
+    cfg = fm.LayerConfig(H=256, I=128, E=8, n_shared=1, n_group=1, topk_group=1, topk=2,
+                         afmt="bf16", wfmt="mx", block_m=16, fragment_layout=False)
+    lay = fm.MoELayer(cfg, {}, device="cpu")
+    sizes = list(range(1, L.MAX_CACHED_BATCH_SIZES + 5))
+    for T in sizes:
+        b = lay._buffers(T)
+        assert b["h"].shape == (T * 3, 128) and b["out"].shape == (T, 256)
+    assert list(lay._bufs) == sizes[-L.MAX_CACHED_BATCH_SIZES:]
+    again = lay._buffers(sizes[-L.MAX_CACHED_BATCH_SIZES])     # a hit moves to the back
+    assert again is lay._bufs[sizes[-L.MAX_CACHED_BATCH_SIZES]]
+    assert list(lay._bufs)[-1] == sizes[-L.MAX_CACHED_BATCH_SIZES]
