@@ -15,6 +15,7 @@ import oracle.convert as OC
 import oracle.formats as OF
 import oracle.gemm as OG
 import oracle.layer as OL
+import oracle.permute as OP
 import oracle.quant as OQ
 import oracle.route as OR
 
@@ -28,6 +29,13 @@ _orig_round = OF.round_to_grid
 _orig_silu = OG.silu_mul
 _orig_act = OL.activation_values
 _orig_fp8q = OQ.fp8_quant_per_token
+_orig_sigmoid = OR.sigmoid_fp32
+_orig_route_token = OR.route_token
+_orig_e4m3 = OF.e4m3_decode
+_orig_mxdq = OF.mxfp4_dequant
+_orig_nvdq = OF.nvfp4_dequant
+_orig_combine = OG.moe_combine
+_orig_permute = OP.moe_permute
 
 
 def _fp8_scale_per_tensor(x_bits):
@@ -64,6 +72,77 @@ def _round_ties_away(x, mbits, emin, maxval, saturate):
     return np.where(tie, up, r)
 
 
+def _combine_without_shared(y_sorted, pair_pos, topk_w, T, topk, n_shared):
+    pos = np.asarray(pair_pos).reshape(T, topk + n_shared).copy()
+    pos[:, topk:] = -1
+    return _orig_combine(y_sorted, pos.reshape(-1), topk_w, T, topk, n_shared)
+
+
+def _combine_shared_weighted(y_sorted, pair_pos, topk_w, T, topk, n_shared):
+    """The shared slot scaled by the first routing weight instead of 1."""
+    out, _ = _orig_combine(y_sorted, pair_pos, topk_w, T, topk, n_shared)
+    pos = np.asarray(pair_pos).reshape(T, topk + n_shared)
+    w = np.asarray(topk_w, dtype=np.float64).reshape(T, topk)
+    for t in range(T):
+        for i in range(n_shared):
+            p = pos[t, topk + i]
+            if p >= 0:
+                out[t] += (w[t, 0] - 1.0) * y_sorted[p]
+    return out, OF.bf16_bits(out)
+
+
+def _permute_unstable(topk_ids, E, n_shared, block_m):
+    """Pairs of one expert in descending pair order."""
+    r = _orig_permute(topk_ids, E, n_shared, block_m)
+    sp = r["sorted_pairs"].copy()
+    offs = r["expert_offsets"]
+    for e in range(len(offs) - 1):
+        sp[offs[e]:offs[e + 1]] = sp[offs[e]:offs[e + 1]][::-1]
+    pp = np.full_like(r["pair_pos"], -1)
+    for i, q in enumerate(sp):
+        if q >= 0:
+            pp[q] = i
+    return dict(r, sorted_pairs=sp, pair_pos=pp)
+
+
+def _permute_tiles_unpadded(topk_ids, E, n_shared, block_m):
+    """Tiles cut from all sorted rows at once, not per expert."""
+    r = _orig_permute(topk_ids, E, n_shared, block_m)
+    n = int(r["expert_offsets"][-1])
+    offs = r["expert_offsets"]
+    tiles = []
+    for t0 in range(0, n, block_m):
+        e = int(np.searchsorted(offs, t0, side="right") - 1)
+        tiles.append((e, (t0 - int(offs[e])) // block_m))
+    tiles = np.array(tiles, dtype=np.int32).reshape(-1, 2)
+    return dict(r, tiles=tiles, n_tiles=len(tiles))
+
+
+def _route_top1_group_score(logit_row, bias, n_group, topk_group, topk, renormalize=True,
+                            routed_scale=1.0):
+    """Groups ranked by their single largest key."""
+    E = len(logit_row)
+    s = OR.sigmoid_fp32(logit_row)
+    key = (s + np.asarray(bias, dtype=np.float32)).astype(np.float32)
+    allowed = np.ones(E, dtype=bool)
+    if n_group > 1:
+        G = E // n_group
+        gscore = np.array([key[g * G:(g + 1) * G].max() for g in range(n_group)], np.float32)
+        allowed[:] = False
+        for g in OR._order_desc(gscore)[:topk_group]:
+            allowed[g * G:(g + 1) * G] = True
+    cand = np.nonzero(allowed)[0]
+    ids = cand[OR._order_desc(key[cand])][:topk].astype(np.int32)
+    sel = s[ids].astype(np.float64)
+    w = sel / sel.sum() if renormalize else sel.copy()
+    return ids, w * float(routed_scale)
+
+
+def _route_unscaled(logit_row, bias, n_group, topk_group, topk, renormalize=True,
+                    routed_scale=1.0):
+    return _orig_route_token(logit_row, bias, n_group, topk_group, topk, renormalize, 1.0)
+
+
 def _order_desc_high_first(values):
     idx = np.arange(len(values))
     return np.lexsort((-idx, -values.astype(np.float64)))
@@ -90,6 +169,22 @@ MUTANTS = {
                                                         _fp8_scale_per_tensor)],
     "gate/up swapped": [(OG, "silu_mul", lambda gu, I: _orig_silu(
         np.concatenate([gu[:, I:], gu[:, :I]], axis=1), I))],
+    "sigmoid of +logit": [(OR, "sigmoid_fp32",
+                           lambda l: _orig_sigmoid(-np.asarray(l, dtype=np.float32)))],
+    "group score = largest key only": [(OR, "route_token", _route_top1_group_score)],
+    "routed_scale ignored": [(OR, "route_token", _route_unscaled)],
+    "E4M3 bias 8": [(OF, "e4m3_decode", lambda c: _orig_e4m3(c) * 0.5)],
+    "NVFP4 tensor scale ignored": [(OF, "nvfp4_dequant", lambda p, s, ts: _orig_nvdq(p, s, 1.0))],
+    "MX scale of the neighbouring block": [(OF, "mxfp4_dequant", lambda p, s: _orig_mxdq(
+        p, np.roll(np.asarray(s), 1, axis=-1)))],
+    "E2M1 code 7 is 5.0": [(OF, "E2M1_MAGNITUDES",
+                            np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 5.0]))],
+    "SiLU sign flipped": [(OG, "silu_mul", lambda gu, I: gu[:, :I] / (1.0 + np.exp(
+        np.clip(gu[:, :I], -700, 700))) * gu[:, I:])],
+    "combine drops the shared expert": [(OG, "moe_combine", _combine_without_shared)],
+    "combine weights the shared expert": [(OG, "moe_combine", _combine_shared_weighted)],
+    "permutation unstable inside an expert": [(OP, "moe_permute", _permute_unstable)],
+    "tiles not padded per expert": [(OP, "moe_permute", _permute_tiles_unpadded)],
 }
 
 PIN_MODULES = [test_oracle_formats, test_oracle_convert, test_oracle_quant,
@@ -119,6 +214,9 @@ def test_mutant_is_killed(mutant, monkeypatch):
         try:
             with np.errstate(all="ignore"):
                 fn()
-        except Exception:
+        except AssertionError:
+            # a failed check; an error raised by the mutant itself does not count
             killed.append(name)
+        except Exception:
+            pass
     assert killed, f"mutant '{mutant}' survived every pin"
