@@ -36,6 +36,9 @@ _orig_mxdq = OF.mxfp4_dequant
 _orig_nvdq = OF.nvfp4_dequant
 _orig_combine = OG.moe_combine
 _orig_permute = OP.moe_permute
+_orig_nvqdq = OQ.nvfp4_qdq
+_orig_e2m1_enc = OF.e2m1_encode
+_orig_convert_row = OC.convert_row
 
 
 def _fp8_scale_per_tensor(x_bits):
@@ -138,6 +141,41 @@ def _route_top1_group_score(logit_row, bias, n_group, topk_group, topk, renormal
     return ids, w * float(routed_scale)
 
 
+def _nvfp4_scale_without_6(x_bits, tensor_scale_in=None):
+    """The dynamic NVFP4 tensor scale amax / 448 (the E2M1 maximum left out)."""
+    if tensor_scale_in is None:
+        x = OF.bf16_decode(x_bits).astype(np.float32)
+        amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+        tensor_scale_in = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    return _orig_nvqdq(x_bits, tensor_scale_in)
+
+
+def _grid_toward_zero(x, mbits, emin, maxval, saturate):
+    """Rounding onto the grid by truncation instead of to nearest even."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, emin)
+    q = np.ldexp(1.0, e - mbits)
+    r = np.where(a == 0, 0.0, np.floor(a / q) * q)
+    r = np.where(r > maxval, maxval if saturate else np.inf, r)
+    return np.copysign(r, x)
+
+
+def _e2m1_saturate_at_4(x):
+    return _orig_e2m1_enc(np.clip(np.asarray(x, dtype=np.float64), -4.0, 4.0))
+
+
+def _convert_nan_blocks_in_max(codes_packed, scales):
+    """Blocks with scale 255 taken into e_max as if their scale were 254."""
+    s = np.asarray(scales).copy()
+    fp8, k, status, inexact = _orig_convert_row(codes_packed, np.where(s == 255, 254, s))
+    nan_blk = np.repeat(s == 255, 32)
+    fp8 = np.where(nan_blk, np.uint8(0x7F), fp8).astype(np.uint8)
+    return fp8, k, (2 if (s == 255).any() else status), inexact
+
+
 def _route_unscaled(logit_row, bias, n_group, topk_group, topk, renormalize=True,
                     routed_scale=1.0):
     return _orig_route_token(logit_row, bias, n_group, topk_group, topk, renormalize, 1.0)
@@ -185,6 +223,13 @@ MUTANTS = {
     "combine weights the shared expert": [(OG, "moe_combine", _combine_shared_weighted)],
     "permutation unstable inside an expert": [(OP, "moe_permute", _permute_unstable)],
     "tiles not padded per expert": [(OP, "moe_permute", _permute_tiles_unpadded)],
+    "NVFP4 tensor scale amax / 448": [(OQ, "nvfp4_qdq", _nvfp4_scale_without_6)],
+    "rounding toward zero on every grid": [(OF, "round_to_grid", _grid_toward_zero)],
+    "E2M1 encode saturates at 4": [(OF, "e2m1_encode", _e2m1_saturate_at_4)],
+    "FP8 per-token scale amax / 240": [(OQ, "FP8_MAX", 240.0)],
+    "E4M3 subnormal quantum 2^-10": [(OF, "e4m3_decode", lambda c: np.where(
+        ((np.asarray(c, dtype=np.int64) >> 3) & 0xF) == 0, 0.5, 1.0) * _orig_e4m3(c))],
+    "NaN blocks counted in the row maximum": [(OC, "convert_row", _convert_nan_blocks_in_max)],
 }
 
 PIN_MODULES = [test_oracle_formats, test_oracle_convert, test_oracle_quant,
